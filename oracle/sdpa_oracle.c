@@ -1,0 +1,208 @@
+/*
+ * Plain fp64 CPU oracle for scaled dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or constant with the
+ * HIP implementation.
+ *
+ * What it computes is the definition itself, written out with no tiling,
+ * no online softmax and no fused steps:
+ *
+ *   Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V
+ *       "Aufmerksamkeit ist alles, was Sie brauchen", section 3.2.1, eq. (1);
+ *       "Attention Is All You Need" (cookipedia), section "Transformer の構造".
+ *
+ * per (batch b, head h, query row i), each (b, h) slice being one instance of
+ * eq. (1) ("all heads in parallel": cookipedia article, "Transformer の構造";
+ * German translation, section 3.2.2).  The row steps follow the proof section
+ * (証明) of the formula page "トランスフォーマーの注意機構":
+ *   1. scores   s_j = (q . k_j) / tau, tau = sqrt(d_k) by default
+ *               (the page's first display; the square root is lost in its
+ *               extraction and restored from the same page's remark that the
+ *               divisor for d_k = 4 is 2, and from eq. (1) of the paper);
+ *   2. weights  a_j = e^{s_j} / sum_i e^{s_i} (second display).  The largest
+ *               score is subtracted first; this leaves every a_j unchanged
+ *               because weights depend only on score differences (fourth
+ *               display, a_j / a_i = e^{s_j - s_i});
+ *   3. output   o = sum_j a_j v_j (third display);
+ *   4. lse      log sum_i e^{s_i}, the smoothed maximum named in the page's
+ *               closing "広がる学問 / 数学" paragraph, returned as m + ln Z.
+ *
+ * Masks (both set a score to -inf before the softmax, so its weight is
+ * exactly 0: formula page, section 応用, "先を読まない仕掛け"):
+ *   causal   key j is valid for query i only if j <= i: the strict upper
+ *            triangle of Q K^T is masked, the diagonal kept (cookipedia
+ *            article, section "原論文でのデコーダ").  Applied top-left aligned
+ *            for any Lq, Lk.
+ *   key_lens key j is valid only if j < clamp(key_lens[b], 0, Lk) (padding of
+ *            variable-length batches; D2L-74-Transformer, "Layer Norm").
+ * A row with no valid key returns o = 0 and lse = -inf.
+ *
+ * Inputs may be fp64, fp32 or bf16 (raw 16-bit patterns); every element is
+ * widened to fp64 exactly before any arithmetic.  Outputs are fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_BF16 = 2 };
+
+/* Exact widening of one stored element to fp64. */
+static double load_elem(const void* base, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_F64) return ((const double*)base)[idx];
+    if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+    /* bf16: the 16 stored bits are the top half of an IEEE binary32. */
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/*
+ * One query row of one (b, h) slice.  `work` holds at least Lk doubles.
+ * q_off, kv_off: element offsets of the row of Q and of the (b, h) slice of
+ * K and V.
+ */
+static void attention_row(const void* q, const void* k, const void* v,
+                          int dtype, int64_t q_off, int64_t kv_off,
+                          int64_t d, int64_t n_valid, double tau,
+                          double* o, double* lse, double* work)
+{
+    if (n_valid <= 0) {
+        for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    /* 1. scores */
+    for (int64_t j = 0; j < n_valid; ++j) {
+        double z = 0.0;
+        for (int64_t t = 0; t < d; ++t)
+            z += load_elem(q, dtype, q_off + t) * load_elem(k, dtype, kv_off + j * d + t);
+        work[j] = z / tau;
+    }
+    /* 2. weights, after subtracting the largest score */
+    double m = work[0];
+    for (int64_t j = 1; j < n_valid; ++j)
+        if (work[j] > m) m = work[j];
+    double Z = 0.0;
+    for (int64_t j = 0; j < n_valid; ++j) {
+        work[j] = exp(work[j] - m);
+        Z += work[j];
+    }
+    for (int64_t j = 0; j < n_valid; ++j) work[j] /= Z;
+    /* 3. output: weighted sum of the value rows */
+    for (int64_t t = 0; t < d; ++t) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < n_valid; ++j)
+            acc += work[j] * load_elem(v, dtype, kv_off + j * d + t);
+        o[t] = acc;
+    }
+    /* 4. log-sum-exp of the valid scores */
+    *lse = m + log(Z);
+}
+
+/* Number of valid keys for query row i of batch b. */
+static int64_t valid_keys(int64_t i, int64_t b, int64_t Lk, int causal,
+                          const int32_t* key_lens)
+{
+    int64_t hi = Lk;
+    if (key_lens) {
+        int64_t len = key_lens[b];
+        if (len < 0) len = 0;
+        if (len < hi) hi = len;
+    }
+    if (causal && i + 1 < hi) hi = i + 1;
+    return hi;
+}
+
+static int check_args(const void* q, const void* k, const void* v, int dtype,
+                      int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                      int causal, double* out, double* lse)
+{
+    if (!q || !k || !v || !out || !lse) return 1;
+    if (dtype < ORACLE_F64 || dtype > ORACLE_BF16) return 1;
+    if (B < 1 || H < 1 || Lq < 1 || Lk < 1 || d < 1) return 1;
+    if (causal != 0 && causal != 1) return 1;
+    return 0;
+}
+
+/*
+ * A chosen set of rows: rows[r] = (b * H + h) * Lq + i.  out is nrows x d,
+ * lse has nrows entries.  tau <= 0 selects tau = sqrt(d).  nthreads <= 0
+ * uses the OpenMP default.  Returns 0 on success, 1 on bad arguments.
+ */
+int oracle_sdpa_rows(const void* q, const void* k, const void* v, int dtype,
+                     int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                     int causal, const int32_t* key_lens, double tau,
+                     const int64_t* rows, int64_t nrows,
+                     double* out, double* lse, int nthreads)
+{
+    if (check_args(q, k, v, dtype, B, H, Lq, Lk, d, causal, out, lse)) return 1;
+    if (nrows < 0 || (nrows > 0 && !rows)) return 1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= B * H * Lq) return 1;
+    if (!(tau > 0.0)) tau = sqrt((double)d);
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    int bad = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* work = (double*)malloc(sizeof(double) * (size_t)Lk);
+        if (!work) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!work) continue;
+            int64_t row = rows[r];
+            int64_t i = row % Lq;
+            int64_t bh = row / Lq;
+            int64_t b = bh / H;
+            int64_t n_valid = valid_keys(i, b, Lk, causal, key_lens);
+            attention_row(q, k, v, dtype, row * d, bh * Lk * d, d, n_valid, tau,
+                          out + r * d, lse + r, work);
+        }
+        free(work);
+    }
+    return bad ? 2 : 0;
+}
+
+/*
+ * Every row.  q and out are [B, H, Lq, d], k and v are [B, H, Lk, d], lse is
+ * [B, H, Lq], all contiguous row-major.
+ */
+int oracle_sdpa(const void* q, const void* k, const void* v, int dtype,
+                int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                int causal, const int32_t* key_lens, double tau,
+                double* out, double* lse, int nthreads)
+{
+    if (check_args(q, k, v, dtype, B, H, Lq, Lk, d, causal, out, lse)) return 1;
+    if (!(tau > 0.0)) tau = sqrt((double)d);
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    const int64_t nrows = B * H * Lq;
+    int bad = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* work = (double*)malloc(sizeof(double) * (size_t)Lk);
+        if (!work) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t row = 0; row < nrows; ++row) {
+            if (!work) continue;
+            int64_t i = row % Lq;
+            int64_t bh = row / Lq;
+            int64_t b = bh / H;
+            int64_t n_valid = valid_keys(i, b, Lk, causal, key_lens);
+            attention_row(q, k, v, dtype, row * d, bh * Lk * d, d, n_valid, tau,
+                          out + row * d, lse + row, work);
+        }
+        free(work);
+    }
+    return bad ? 2 : 0;
+}
