@@ -1,0 +1,120 @@
+/*
+ * sdpa.h -- C ABI of the MI355X (gfx950) scaled dot-product attention forward.
+ *
+ * The operation is eq. (1) of "Aufmerksamkeit ist alles, was Sie brauchen"
+ * (German translation of "Attention Is All You Need"), section 3.2.1:
+ *
+ *     Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V
+ *
+ * applied independently to every (batch b, head h) slice -- "all heads in
+ * parallel" (cookipedia article "Attention Is All You Need", section
+ * "Transformer の構造"; German translation, section 3.2.2).  Three forms are
+ * covered, as listed in "D2L-74-Transformer", section "Attention: 3 different
+ * kinds":
+ *   - encoder self-attention: Lq = Lk, no mask;
+ *   - decoder masked self-attention: causal = 1, the strict upper triangle of
+ *     Q K^T is set to -inf before the softmax, the diagonal is kept
+ *     (cookipedia article, section "原論文でのデコーダ");
+ *   - encoder-decoder cross-attention: Lq != Lk, keys and values from the
+ *     encoder, optionally with per-batch key lengths.
+ *
+ * Plain C types only; all tensor pointers are device pointers owned by the
+ * caller.  The library never allocates, frees or retains caller memory.
+ */
+#ifndef SDPA_MI355X_H_
+#define SDPA_MI355X_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque handle; created by sdpa_create, owned by the library. */
+typedef struct sdpa_ctx* sdpa_handle_t;
+
+typedef enum {
+    SDPA_STATUS_SUCCESS = 0,
+    SDPA_STATUS_INVALID_VALUE = 1,   /* bad handle, pointer, size or flag */
+    SDPA_STATUS_NOT_SUPPORTED = 2,   /* dtype / d_k / device combination not built */
+    SDPA_STATUS_HIP_ERROR = 3,       /* a HIP runtime call or kernel launch failed */
+    SDPA_STATUS_ALLOC_FAILED = 4     /* host allocation of the handle failed */
+} sdpa_status_t;
+
+typedef enum {
+    SDPA_DTYPE_FP32 = 0,   /* q, k, v, out are float; any 1 <= d_k <= 256 */
+    SDPA_DTYPE_BF16 = 1    /* q, k, v, out are bf16 (uint16 bits); d_k in {64, 128} */
+} sdpa_dtype_t;
+
+/*
+ * Create a handle bound to one element type and one HIP device.
+ *   h       out: the new handle (unchanged on error).
+ *   dtype   element type of q, k, v and out for every call on this handle.
+ *   device  HIP device ordinal; must be a gfx950 device for SDPA_DTYPE_BF16.
+ * Reads the device's properties once (architecture, compute-unit count); the
+ * handle is immutable afterwards, so concurrent sdpa_forward calls on
+ * different streams may share it.
+ * Errors: INVALID_VALUE (h == NULL, unknown dtype, bad ordinal),
+ * HIP_ERROR (device query failed), NOT_SUPPORTED (bf16 on a non-gfx950
+ * device), ALLOC_FAILED.
+ */
+sdpa_status_t sdpa_create(sdpa_handle_t* h, sdpa_dtype_t dtype, int device);
+
+/*
+ * Enqueue one attention forward on `stream`; returns without waiting.
+ *
+ *   q        [B, H, Lq, d_k] contiguous row-major, handle's dtype.
+ *   k, v     [B, H, Lk, d_k] contiguous row-major (values have width d_k).
+ *   out      [B, H, Lq, d_k] contiguous, handle's dtype; must not overlap
+ *            q, k or v.  out[b,h,i,:] = sum_j a_ij v[b,h,j,:] with
+ *            a_ij = softmax over the valid j of s_ij = q_i . k_j / sqrt(d_k)
+ *            (German translation, section 3.2.1, eq. (1)).  Results are
+ *            rounded to the output type to nearest, ties to even.
+ *   lse      [B, H, Lq] float, or NULL: natural-log sum over the valid j of
+ *            e^{s_ij} (the smoothed maximum of the scores named in the formula
+ *            page "トランスフォーマーの注意機構", section "広がる学問").
+ *   B, H, Lq, Lk, d_k   sizes, each >= 1.
+ *   causal   0 or 1.  1: key j is valid for query i only if j <= i (top-left
+ *            aligned for any Lq, Lk).
+ *   key_lens device int32[B], or NULL: key j of batch b is valid only if
+ *            j < clamp(key_lens[b], 0, Lk).  Keys and values at or past that
+ *            length are never read, so they may hold any bits.
+ *   stream   HIP stream (hipStream_t) as an opaque pointer; NULL = default.
+ * A query row with no valid key gets out = 0 and lse = -inf.
+ *
+ * Accumulation is fp32 on every path.  bf16: products on bf16 matrix cores
+ * with fp32 accumulation, the softmax weights rounded to bf16 before they
+ * multiply V.
+ *
+ * Errors (returned before anything is enqueued; out and lse untouched):
+ * INVALID_VALUE for a NULL handle or tensor pointer, sizes < 1, causal not
+ * 0/1, overlapping out, or sizes whose element counts overflow int64;
+ * NOT_SUPPORTED for d_k outside the handle dtype's range or bf16 pointers
+ * not 16-byte aligned; HIP_ERROR if the launch fails.  Faults during
+ * execution surface at the caller's next synchronisation, as in HIP.
+ */
+sdpa_status_t sdpa_forward(sdpa_handle_t h,
+                           const void* q, const void* k, const void* v,
+                           void* out, float* lse,
+                           int B, int H, int Lq, int Lk, int d_k,
+                           int causal, const int32_t* key_lens, void* stream);
+
+/* Release a handle (NULL is accepted).  Does not synchronise any stream. */
+sdpa_status_t sdpa_destroy(sdpa_handle_t h);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* sdpa_status_string(sdpa_status_t s);
+
+/*
+ * Tile configuration that sdpa_forward would launch for these arguments,
+ * written as a short static string (e.g. "bf16_d128_bc64_w4"); for logging
+ * and profiling.  Returns NULL when the combination is not supported.
+ */
+const char* sdpa_kernel_name(sdpa_handle_t h, int B, int H, int Lq, int Lk,
+                             int d_k, int causal, int has_key_lens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H_ */

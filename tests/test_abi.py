@@ -1,0 +1,86 @@
+"""The C ABI: the library loads and exports every symbol include/sdpa.h
+declares (CPU), and argument validation returns the documented statuses
+(CPU where no device is needed, GPU otherwise)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_scaled_dot_sdpa_amd import binding as b
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "sdpa.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_exactly_the_bound_symbols():
+    assert declared_functions() == sorted(b.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = b.load_library()
+    for name in declared_functions():
+        assert getattr(lib, name) is not None, name
+    # and the exported dynamic symbols really are C (unmangled) names
+    out = os.popen(f"nm -D --defined-only {b.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_status_strings():
+    for code, name in [(0, "SUCCESS"), (1, "INVALID_VALUE"), (2, "NOT_SUPPORTED"),
+                       (3, "HIP_ERROR"), (4, "ALLOC_FAILED")]:
+        assert b.status_string(code) == f"SDPA_STATUS_{name}"
+    assert b.status_string(99) == "SDPA_STATUS_UNKNOWN"
+
+
+def test_null_handle_and_pointers_rejected_without_device():
+    st = b.sdpa_forward(None, 16, 16, 16, 16, None, 1, 1, 1, 1, 64, 0, None, None)
+    assert st == b.INVALID_VALUE
+    lib = b.load_library()
+    assert lib.sdpa_create(None, 1, 0) == b.INVALID_VALUE
+    h = ctypes.c_void_p()
+    assert lib.sdpa_create(ctypes.byref(h), 7, 0) == b.INVALID_VALUE
+    assert lib.sdpa_destroy(None) == b.SUCCESS
+    assert b.sdpa_kernel_name(None, 1, 1, 1, 1, 64, 0, 0) is None
+
+
+@pytest.mark.gpu
+def test_validation_statuses_on_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    h = b.handle_for(b.DTYPE_BF16, 0)
+    x = torch.zeros(2, 2, 64, 128, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros_like(x)
+    o = torch.zeros_like(x)
+    p = lambda t: t.data_ptr()
+    fwd = lambda **kw: b.sdpa_forward(**{**dict(handle=h, q=p(x), k=p(y), v=p(y), out=p(o), lse=None,
+                                                 B=2, H=2, Lq=64, Lk=64, d_k=128, causal=0,
+                                                 key_lens=None, stream=None), **kw})
+    assert fwd() == b.SUCCESS
+    torch.cuda.synchronize()
+    assert fwd(q=None) == b.INVALID_VALUE
+    assert fwd(out=None) == b.INVALID_VALUE
+    assert fwd(B=0) == b.INVALID_VALUE
+    assert fwd(Lk=-1) == b.INVALID_VALUE
+    assert fwd(causal=2) == b.INVALID_VALUE
+    assert fwd(out=p(x)) == b.INVALID_VALUE               # out aliases q
+    assert fwd(out=p(y) + 256) == b.INVALID_VALUE         # out overlaps k
+    assert fwd(d_k=96) == b.NOT_SUPPORTED
+    assert fwd(d_k=64, q=p(x) + 2) == b.NOT_SUPPORTED     # misaligned bf16
+    assert fwd(B=1 << 30, H=1 << 30) == b.INVALID_VALUE   # element count overflow
+    assert b.sdpa_kernel_name(h, 4, 96, 4096, 4096, 128, 1, 0).startswith("bf16_d128")
+    hf = b.handle_for(b.DTYPE_FP32, 0)
+    xf = torch.zeros(1, 1, 4, 300, device="cuda")
+    of = torch.zeros_like(xf)
+    assert b.sdpa_forward(hf, p(xf), p(xf), p(xf), p(of), None, 1, 1, 4, 4, 300, 0, None,
+                          None) == b.NOT_SUPPORTED
+    with pytest.raises(b.SdpaError):
+        b.forward(x[..., :96].contiguous(), y[..., :96].contiguous(), y[..., :96].contiguous())

@@ -1,0 +1,259 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Inputs come from the seeded generators; expected values only from the oracle.
+Tolerances (max-abs): output 1e-5 for fp32, 2e-2 for bf16; lse 1e-3.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import (announce, assert_close, generate, oracle_ref, require_gpu, run_gpu,
+                      TOL_OUT)
+from transformer_scaled_dot_sdpa_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ---------------------------------------------------------------- workloads
+@pytest.mark.parametrize("name", ["toy_f32", "encoder_d64", "decoder_causal_d64", "cross_padded_d64"])
+def test_named_workload_full(name):
+    w = inputs.WORKLOADS[name]
+    announce(f"{name}: B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} d{w.d} {w.dtype} causal={w.causal} seed={w.seed}")
+    q, k, v, kl = inputs.generate_workload(w)
+    o, l = run_gpu(q, k, v, w.dtype, w.causal, kl)
+    ro, rl = oracle_ref(q, k, v, w.dtype, w.causal, kl)
+    assert_close(o, l, ro, rl, w.dtype, name)
+
+
+@pytest.fixture(scope="module")
+def large_run():
+    """The large causal workload at full size, run once in the benchmark's
+    launch configuration."""
+    require_gpu()
+    w = inputs.WORKLOADS["large_causal_d128"]
+    announce(f"large_causal_d128 full size: generating seed={w.seed}")
+    q, k, v, kl = inputs.generate_workload(w)
+    announce("large_causal_d128: running sdpa_forward")
+    o, l = run_gpu(q, k, v, w.dtype, w.causal, kl)
+    return w, q, k, v, o, l
+
+
+def test_large_workload_sampled_rows(large_run):
+    import oracle
+    w, q, k, v, o, l = large_run
+    rng = np.random.default_rng(1234)
+    fixed_i = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 1000, 2047, 2048, 4094, 4095]
+    rows = []
+    for b in range(w.B):
+        for hh in sorted(set([0, w.H - 1] + list(rng.integers(0, w.H, size=3)))):
+            base = (b * w.H + hh) * w.Lq
+            rows += [base + i for i in fixed_i]
+            rows += [base + int(i) for i in rng.integers(0, w.Lq, size=8)]
+    rows = np.array(sorted(set(rows)), dtype=np.int64)
+    ro, rl = oracle.sdpa_rows(q, k, v, rows, causal=True, bf16=True)
+    og = o.reshape(-1, w.d)[rows]
+    lg = l.reshape(-1)[rows]
+    assert_close(og, lg, ro, rl, "bf16", f"large_causal_d128 {rows.size} sampled rows")
+    # relative error check on the small late-row outputs as well
+    rel = np.linalg.norm(og - ro) / np.linalg.norm(ro)
+    assert rel < 1e-2, rel
+
+
+def test_large_workload_row0_is_v0(large_run):
+    """Causal row 0 attends only key 0 with weight exactly 1: O = V[0] bitwise."""
+    w, q, k, v, o, l = large_run
+    v0 = inputs.bf16_bits_to_f32(v[:, :, 0])
+    assert np.array_equal(o[:, :, 0], v0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+# ---------------------------------------------------------- ragged / edges
+EDGE_BF16 = [
+    # B, H, Lq, Lk, causal, key_lens
+    (1, 1, 1, 1, False, None),
+    (1, 1, 1, 1, True, None),
+    (2, 3, 7, 7, False, None),
+    (2, 3, 7, 7, True, None),
+    (1, 2, 33, 65, False, None),
+    (1, 2, 129, 129, True, None),
+    (2, 2, 200, 300, False, None),
+    (2, 2, 300, 200, True, None),       # causal with Lq > Lk (top-left aligned)
+    (2, 2, 150, 333, True, None),       # causal with Lq < Lk
+    (3, 2, 64, 64, False, [0, 1, 64]),  # empty row, single key, full
+    (4, 2, 130, 257, False, [5, 129, 1000, -3]),  # clamp above Lk and below 0
+    (2, 2, 257, 257, True, [100, 257]),
+    (1, 1, 512, 512, True, None),
+]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", EDGE_BF16, ids=lambda c: "B{}H{}q{}k{}c{}L{}".format(*c[:5], c[5]))
+def test_bf16_edges(d, case):
+    B, H, Lq, Lk, causal, kl = case
+    seed = 100 + d + Lq + 7 * Lk
+    announce(f"bf16 edge d{d} B{B} H{H} Lq{Lq} Lk{Lk} causal={causal} key_lens={kl} seed={seed}")
+    q, k, v, _ = generate(B, H, Lq, Lk, d, "bf16", seed)
+    o, l = run_gpu(q, k, v, "bf16", causal, kl)
+    ro, rl = oracle_ref(q, k, v, "bf16", causal, kl)
+    assert_close(o, l, ro, rl, "bf16", f"d{d} {case}")
+    if kl is not None:
+        for b, n in enumerate(kl):
+            if n <= 0:
+                assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+
+
+EDGE_F32 = [
+    # B, H, Lq, Lk, d, causal, key_lens
+    (1, 2, 8, 8, 3, False, None),
+    (1, 2, 4, 4, 3, True, None),     # toy decoder self-attention
+    (1, 2, 4, 8, 3, False, None),    # toy cross-attention
+    (2, 2, 65, 130, 1, False, None),
+    (2, 3, 70, 70, 16, True, [70, 3]),
+    (2, 2, 33, 200, 100, False, [0, 150]),
+    (2, 1, 40, 50, 128, True, None),
+    (1, 1, 20, 129, 256, False, None),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_F32, ids=lambda c: "B{}H{}q{}k{}d{}c{}".format(*c[:6]))
+def test_f32_edges(case):
+    B, H, Lq, Lk, d, causal, kl = case
+    if kl is not None:
+        kl = (list(kl) * B)[:B]
+    seed = 7 + Lq + Lk + d
+    announce(f"fp32 edge B{B} H{H} Lq{Lq} Lk{Lk} d{d} causal={causal} key_lens={kl} seed={seed}")
+    q, k, v, _ = generate(B, H, Lq, Lk, d, "fp32", seed)
+    o, l = run_gpu(q, k, v, "fp32", causal, kl)
+    ro, rl = oracle_ref(q, k, v, "fp32", causal, kl)
+    assert_close(o, l, ro, rl, "fp32", f"fp32 {case}")
+
+
+# ------------------------------------------------------- properties on GPU
+def test_padding_contents_never_read():
+    """Poisoning K/V at and past key_lens with NaN / 1e30 changes nothing."""
+    B, H, Lq, Lk, d = 3, 2, 70, 200, 64
+    q, k, v, _ = generate(B, H, Lq, Lk, d, "bf16", 5)
+    kl = [37, 200, 129]
+    announce(f"padding poison d{d} key_lens={kl}")
+    o1, l1 = run_gpu(q, k, v, "bf16", False, kl)
+    kp, vp = k.copy(), v.copy()
+    for b, n in enumerate(kl):
+        kp[b, :, n:] = 0x7FC0          # NaN
+        vp[b, :, n:] = 0x7149          # ~1e30
+    o2, l2 = run_gpu(q, kp, vp, "bf16", False, kl)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bitwise_deterministic(causal):
+    q, k, v, _ = generate(2, 4, 300, 300, 128, "bf16", 6)
+    announce(f"determinism d128 L300 causal={causal}")
+    a = run_gpu(q, k, v, "bf16", causal)
+    b = run_gpu(q, k, v, "bf16", causal)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_head_batch_permutation_equivariance():
+    B, H, L, d = 3, 4, 96, 64
+    q, k, v, _ = generate(B, H, L, L, d, "bf16", 8)
+    announce("permutation equivariance d64")
+    o, l = run_gpu(q, k, v, "bf16", True)
+    perm = np.random.default_rng(0).permutation(B * H)
+    pq = q.reshape(B * H, L, d)[perm].reshape(B, H, L, d)
+    pk = k.reshape(B * H, L, d)[perm].reshape(B, H, L, d)
+    pv = v.reshape(B * H, L, d)[perm].reshape(B, H, L, d)
+    o2, l2 = run_gpu(pq, pk, pv, "bf16", True)
+    assert np.array_equal(o2.reshape(B * H, L, d), o.reshape(B * H, L, d)[perm])
+    assert np.array_equal(l2.reshape(B * H, L), l.reshape(B * H, L)[perm])
+
+
+def test_bf16_two_key_example_d64():
+    """Formula page, section 応用 (d_k = 64): scores 8 apart give weights
+    0.731 / 0.269 after dividing by sqrt(64); scaling q by 8 (undoing the
+    division) gives 0.9997 / 0.0003.  With V rows e_0, e_1 the output is the
+    weight vector.  All inputs are exact in bf16."""
+    d = 64
+    to_bits = inputs.f32_to_bf16_bits
+    q = np.zeros((1, 1, 1, d), np.float32); q[0, 0, 0, 0] = 8.0
+    k = np.zeros((1, 1, 2, d), np.float32); k[0, 0, 0, 0] = 1.0
+    v = np.zeros((1, 1, 2, d), np.float32); v[0, 0, 0, 0] = 1.0; v[0, 0, 1, 1] = 1.0
+    announce("two-key d64 example")
+    o, _ = run_gpu(to_bits(q), to_bits(k), to_bits(v), "bf16")
+    assert abs(o[0, 0, 0, 0] - 0.731) < 5e-3 and abs(o[0, 0, 0, 1] - 0.269) < 5e-3
+    o, _ = run_gpu(to_bits(q * 8), to_bits(k), to_bits(v), "bf16")
+    assert abs(o[0, 0, 0, 0] - 0.9997) < 2e-3 and abs(o[0, 0, 0, 1] - 0.0003) < 2e-3
+
+
+def test_f32_worked_example_and_temperature():
+    """Formula page, section 応用: d_k = 4 example through the fp32 kernel:
+    output (0.70, 1.44, 0.28, 0.26), exp-sum 31.68; fish weight 0.932 when
+    the scores are not divided (q x 2) and 0.217 when divided by 8 (q / 4)."""
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json"),
+                       encoding="utf-8"))
+    keys = np.array(g["keys"], np.float32).reshape(1, 1, 8, 4)
+    q = np.array(g["query"], np.float32).reshape(1, 1, 1, 4)
+    announce("worked example d4 fp32")
+    o, l = run_gpu(q, keys, keys, "fp32")
+    assert np.max(np.abs(o[0, 0, 0] - np.array(g["printed"]["output"]["value"]))) <= 0.005
+    assert abs(np.exp(l[0, 0, 0]) - 31.68) <= 0.005
+    # weights via V = identity (keys padded with zeros to width 8)
+    kp = np.zeros((1, 1, 8, 8), np.float32); kp[..., :4] = keys
+    vp = np.eye(8, dtype=np.float32).reshape(1, 1, 8, 8)
+    fish = g["tokens"].index("魚")
+    for mult, want in ((2.0 * np.sqrt(8) / 2, 0.932), (np.sqrt(8) / 2 / 4, 0.217), (np.sqrt(8) / 2, 0.634)):
+        qp = np.zeros((1, 1, 1, 8), np.float32); qp[..., :4] = q * mult
+        o, _ = run_gpu(qp, kp, vp, "fp32")
+        assert abs(o[0, 0, 0, fish] - want) <= 5e-4 + 1e-5, (mult, o[0, 0, 0])
+
+
+def test_bf16_mean_when_query_zero():
+    """q = 0: every weight is 1/n, the output is the mean of the valid value
+    rows and lse = ln n (temperature limit, formula page section 証明)."""
+    B, H, L, d = 2, 2, 300, 128
+    _, k, v, _ = generate(B, H, L, L, d, "bf16", 9)
+    q = np.zeros((B, H, L, d), np.uint16)
+    kl = [300, 77]
+    announce("query zero -> mean of V")
+    o, l = run_gpu(q, k, v, "bf16", False, kl)
+    vf = inputs.bf16_bits_to_f32(v).astype(np.float64)
+    for b, n in enumerate(kl):
+        mean = vf[b, :, :n].mean(axis=1)  # [H, d]
+        assert np.max(np.abs(o[b] - mean[:, None, :])) < TOL_OUT["bf16"]
+        assert np.max(np.abs(l[b] - np.log(n))) < 1e-5
+
+
+def test_bf16_shift_invariance():
+    """K + 1 u^T: outputs unchanged, lse shifted by q.u / sqrt(d) (formula
+    page section 証明, ratio identity).  Dyadic inputs keep K + u exact."""
+    B, H, Lq, Lk, d = 1, 2, 96, 160, 64
+    rng = np.random.default_rng(10)
+    qf = (rng.integers(-8, 8, size=(B, H, Lq, d)) / 16.0).astype(np.float32)
+    kf = (rng.integers(-8, 8, size=(B, H, Lk, d)) / 16.0).astype(np.float32)
+    vf = rng.standard_normal((B, H, Lk, d)).astype(np.float32)
+    u = (rng.integers(-8, 8, size=d) / 8.0).astype(np.float32)
+    to_bits = inputs.f32_to_bf16_bits
+    announce("shift invariance d64")
+    o1, l1 = run_gpu(to_bits(qf), to_bits(kf), to_bits(vf), "bf16", True)
+    o2, l2 = run_gpu(to_bits(qf), to_bits(kf + u), to_bits(vf), "bf16", True)
+    assert np.max(np.abs(o2 - o1)) < TOL_OUT["bf16"]
+    shift = (qf.astype(np.float64) @ u.astype(np.float64)) / np.sqrt(d)
+    assert np.max(np.abs(l2 - l1 - shift)) < 1e-3
+
+
+def test_bf16_weights_are_a_distribution():
+    """V = identity (Lk <= d): each output row is that query's weight row:
+    positive, summing to 1, and zero on masked keys."""
+    B, H, L, d = 1, 2, 64, 64
+    q, k, _, _ = generate(B, H, L, L, d, "bf16", 11)
+    v = inputs.f32_to_bf16_bits(np.broadcast_to(np.eye(L, d, dtype=np.float32), (B, H, L, d)).copy())
+    announce("weights as distribution d64 causal")
+    o, _ = run_gpu(q, k, v, "bf16", True)
+    assert np.all(np.abs(o.sum(axis=-1) - 1.0) < 2e-2)
+    tri = np.triu(np.ones((L, L), bool), 1)
+    assert np.all(o[:, :, tri] == 0)
+    assert np.all(o[:, :, ~tri] > 0)

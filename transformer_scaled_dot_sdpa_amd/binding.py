@@ -1,0 +1,178 @@
+"""ctypes binding of the C ABI in ``include/sdpa.h``.
+
+Argument marshalling only: tensors are checked and their device pointers and
+the current HIP stream are passed to ``sdpa_forward``; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+
+PyTorch provides device memory and streams and nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libsdpa_mi355x.so")
+
+SUCCESS, INVALID_VALUE, NOT_SUPPORTED, HIP_ERROR, ALLOC_FAILED = 0, 1, 2, 3, 4
+DTYPE_FP32, DTYPE_BF16 = 0, 1
+
+# Every symbol include/sdpa.h declares.
+EXPORTED = ("sdpa_create", "sdpa_forward", "sdpa_destroy", "sdpa_status_string",
+            "sdpa_kernel_name")
+
+
+class SdpaError(RuntimeError):
+    """A non-success status from the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+_lock = threading.Lock()
+_lib = None
+_handles: dict = {}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"HIP library not found at {path}; build it with "
+                    "`python -m transformer_scaled_dot_sdpa_amd.build`")
+            lib = ctypes.CDLL(path)
+            vp, i32 = ctypes.c_void_p, ctypes.c_int
+            lib.sdpa_create.argtypes = [ctypes.POINTER(vp), i32, i32]
+            lib.sdpa_create.restype = i32
+            lib.sdpa_forward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                         i32, vp, vp]
+            lib.sdpa_forward.restype = i32
+            lib.sdpa_destroy.argtypes = [vp]
+            lib.sdpa_destroy.restype = i32
+            lib.sdpa_status_string.argtypes = [i32]
+            lib.sdpa_status_string.restype = ctypes.c_char_p
+            lib.sdpa_kernel_name.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
+            lib.sdpa_kernel_name.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().sdpa_status_string(int(status)).decode()
+
+
+def sdpa_create(dtype: int, device: int) -> int:
+    """Raw ``sdpa_create``: returns the handle as an integer."""
+    h = ctypes.c_void_p()
+    st = load_library().sdpa_create(ctypes.byref(h), int(dtype), int(device))
+    if st != SUCCESS:
+        raise SdpaError(st, "sdpa_create")
+    return h.value
+
+
+def sdpa_destroy(handle: int) -> None:
+    st = load_library().sdpa_destroy(handle)
+    if st != SUCCESS:
+        raise SdpaError(st, "sdpa_destroy")
+
+
+def sdpa_forward(handle, q, k, v, out, lse, B, H, Lq, Lk, d_k, causal, key_lens, stream) -> int:
+    """Raw ``sdpa_forward`` on integer pointers; returns the status code."""
+    return load_library().sdpa_forward(handle, q, k, v, out, lse, int(B), int(H), int(Lq),
+                                       int(Lk), int(d_k), int(causal), key_lens, stream)
+
+
+def sdpa_kernel_name(handle, B, H, Lq, Lk, d_k, causal, has_key_lens):
+    r = load_library().sdpa_kernel_name(handle, int(B), int(H), int(Lq), int(Lk), int(d_k),
+                                        int(causal), int(has_key_lens))
+    return r.decode() if r is not None else None
+
+
+def handle_for(dtype: int, device: int) -> int:
+    """A cached handle per (dtype, device)."""
+    key = (int(dtype), int(device))
+    with _lock:
+        h = _handles.get(key)
+    if h is None:
+        h = sdpa_create(dtype, device)
+        with _lock:
+            _handles[key] = h
+    return h
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def forward(q, k, v, causal: bool = False, key_lens=None, out=None, lse=None,
+            need_lse: bool = True, stream=None):
+    """softmax(q k^T / sqrt(d_k)) v for every (batch, head), on the GPU.
+
+    q: [B, H, Lq, d_k]; k, v: [B, H, Lk, d_k]; contiguous CUDA/HIP tensors of
+    one dtype (bfloat16 or float32) on one device.  ``key_lens``: int32 [B]
+    on the same device, or None.  ``out`` / ``lse`` may be given
+    preallocated.  Enqueued on ``stream`` (default: the current stream).
+    Returns ``(out, lse)``; ``lse`` is None when ``need_lse`` is False and no
+    ``lse`` tensor was given.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, L, d_k], got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, Lq, d = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    Lk = k.shape[2]
+    code = _dtype_code(q)
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must match q in shape, dtype and device, and be contiguous")
+    if lse is None and need_lse:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, Lq) or lse.dtype != torch.float32
+                            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be float32 [B, H, Lq] on q's device")
+    kl_ptr = None
+    if key_lens is not None:
+        if (key_lens.dtype != torch.int32 or key_lens.shape != (B,) or key_lens.device != q.device
+                or not key_lens.is_contiguous()):
+            raise ValueError("key_lens must be a contiguous int32 [B] tensor on q's device")
+        kl_ptr = key_lens.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = sdpa_forward(handle_for(code, dev), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                      out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                      B, H, Lq, Lk, d, int(bool(causal)), kl_ptr, stream.cuda_stream)
+    if st != SUCCESS:
+        raise SdpaError(st, "sdpa_forward")
+    return out, lse
+
+
+def kernel_name(q, k, causal: bool = False, has_key_lens: bool = False):
+    """Tile configuration the library would launch for these tensors."""
+    import torch
+    B, H, Lq, d = q.shape
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    return sdpa_kernel_name(handle_for(_dtype_code(q), dev), B, H, Lq, k.shape[2], d,
+                            int(bool(causal)), int(bool(has_key_lens)))

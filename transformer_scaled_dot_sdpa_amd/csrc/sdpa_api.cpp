@@ -1,0 +1,154 @@
+// C ABI of the attention forward (declared in include/sdpa.h): handle
+// management, argument validation and dispatch to the HIP kernels.
+#include "sdpa.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "sdpa_internal.h"
+
+struct sdpa_ctx {
+    sdpa_dtype_t dtype;
+    int device;
+    int num_cus;
+    char arch[64];
+};
+
+namespace {
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// a * b * c * d without overflowing int64 (all factors >= 1).
+bool mul_fits(long long a, long long b, long long c, long long d, long long* r) {
+    long long x = a;
+    for (long long f : {b, c, d}) {
+        if (x > INT64_MAX / f) return false;
+        x *= f;
+    }
+    *r = x;
+    return true;
+}
+
+bool is_gfx950(const char* arch) { return strncmp(arch, "gfx950", 6) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+sdpa_status_t sdpa_create(sdpa_handle_t* h, sdpa_dtype_t dtype, int device) {
+    if (h == nullptr) return SDPA_STATUS_INVALID_VALUE;
+    if (dtype != SDPA_DTYPE_FP32 && dtype != SDPA_DTYPE_BF16) return SDPA_STATUS_INVALID_VALUE;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    if (device < 0 || device >= count) return SDPA_STATUS_INVALID_VALUE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    if (dtype == SDPA_DTYPE_BF16 && !is_gfx950(prop.gcnArchName)) return SDPA_STATUS_NOT_SUPPORTED;
+    sdpa_ctx* c = new (std::nothrow) sdpa_ctx;
+    if (c == nullptr) return SDPA_STATUS_ALLOC_FAILED;
+    c->dtype = dtype;
+    c->device = device;
+    c->num_cus = prop.multiProcessorCount;
+    strncpy(c->arch, prop.gcnArchName, sizeof(c->arch) - 1);
+    c->arch[sizeof(c->arch) - 1] = '\0';
+    *h = c;
+    return SDPA_STATUS_SUCCESS;
+}
+
+sdpa_status_t sdpa_destroy(sdpa_handle_t h) {
+    delete h;
+    return SDPA_STATUS_SUCCESS;
+}
+
+const char* sdpa_status_string(sdpa_status_t s) {
+    switch (s) {
+        case SDPA_STATUS_SUCCESS: return "SDPA_STATUS_SUCCESS";
+        case SDPA_STATUS_INVALID_VALUE: return "SDPA_STATUS_INVALID_VALUE";
+        case SDPA_STATUS_NOT_SUPPORTED: return "SDPA_STATUS_NOT_SUPPORTED";
+        case SDPA_STATUS_HIP_ERROR: return "SDPA_STATUS_HIP_ERROR";
+        case SDPA_STATUS_ALLOC_FAILED: return "SDPA_STATUS_ALLOC_FAILED";
+    }
+    return "SDPA_STATUS_UNKNOWN";
+}
+
+const char* sdpa_kernel_name(sdpa_handle_t h, int B, int H, int Lq, int Lk, int d_k,
+                             int causal, int has_key_lens) {
+    (void)has_key_lens;
+    if (h == nullptr || B < 1 || H < 1 || Lq < 1 || Lk < 1 || d_k < 1) return nullptr;
+    if (h->dtype == SDPA_DTYPE_FP32) return d_k <= 256 ? "f32_wave_per_row" : nullptr;
+    sdpa::Bf16Tile t;
+    if (!sdpa::select_bf16_tile(d_k, causal, (long long)B * H, Lq, Lk, h->num_cus, &t)) return nullptr;
+    return t.name;
+}
+
+sdpa_status_t sdpa_forward(sdpa_handle_t h, const void* q, const void* k, const void* v,
+                           void* out, float* lse, int B, int H, int Lq, int Lk, int d_k,
+                           int causal, const int32_t* key_lens, void* stream) {
+    if (h == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+        return SDPA_STATUS_INVALID_VALUE;
+    if (B < 1 || H < 1 || Lq < 1 || Lk < 1 || d_k < 1) return SDPA_STATUS_INVALID_VALUE;
+    if (causal != 0 && causal != 1) return SDPA_STATUS_INVALID_VALUE;
+    long long nq = 0, nkv = 0;
+    if (!mul_fits(B, H, Lq, d_k, &nq) || !mul_fits(B, H, Lk, d_k, &nkv))
+        return SDPA_STATUS_INVALID_VALUE;
+    const size_t esz = h->dtype == SDPA_DTYPE_BF16 ? 2 : 4;
+    if ((unsigned long long)nq > SIZE_MAX / esz || (unsigned long long)nkv > SIZE_MAX / esz)
+        return SDPA_STATUS_INVALID_VALUE;
+    const size_t bq = (size_t)nq * esz, bkv = (size_t)nkv * esz;
+    if (overlaps(out, bq, q, bq) || overlaps(out, bq, k, bkv) || overlaps(out, bq, v, bkv))
+        return SDPA_STATUS_INVALID_VALUE;
+    if (lse != nullptr) {
+        const size_t bl = (size_t)B * H * Lq * sizeof(float);
+        if (overlaps(lse, bl, out, bq) || overlaps(lse, bl, q, bq) || overlaps(lse, bl, k, bkv) ||
+            overlaps(lse, bl, v, bkv))
+            return SDPA_STATUS_INVALID_VALUE;
+        if (reinterpret_cast<uintptr_t>(lse) % alignof(float) != 0) return SDPA_STATUS_INVALID_VALUE;
+    }
+
+    sdpa::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.key_lens = key_lens;
+    a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk; a.d = d_k; a.causal = causal;
+
+    sdpa::Bf16Tile tile;
+    if (h->dtype == SDPA_DTYPE_BF16) {
+        if (!sdpa::select_bf16_tile(d_k, causal, (long long)B * H, Lq, Lk, h->num_cus, &tile))
+            return SDPA_STATUS_NOT_SUPPORTED;
+        for (const void* p : {q, k, v, (const void*)out})
+            if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return SDPA_STATUS_NOT_SUPPORTED;
+    } else {
+        if (d_k > 256) return SDPA_STATUS_NOT_SUPPORTED;
+        for (const void* p : {q, k, v, (const void*)out})
+            if (reinterpret_cast<uintptr_t>(p) % alignof(float) != 0) return SDPA_STATUS_INVALID_VALUE;
+    }
+    if (key_lens != nullptr && reinterpret_cast<uintptr_t>(key_lens) % alignof(int32_t) != 0)
+        return SDPA_STATUS_INVALID_VALUE;
+
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    if (cur != h->device && hipSetDevice(h->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = h->dtype == SDPA_DTYPE_BF16 ? sdpa::launch_fwd_bf16(a, tile, s)
+                                               : sdpa::launch_fwd_f32(a, s);
+    if (cur != h->device) (void)hipSetDevice(cur);
+    return e == hipSuccess ? SDPA_STATUS_SUCCESS : SDPA_STATUS_HIP_ERROR;
+}
+
+}  // extern "C"

@@ -1,0 +1,355 @@
+// Fused scaled dot-product attention forward, bf16 in / fp32 accumulate,
+// for gfx950 (CDNA4) matrix cores.
+//
+// Computes, for every (batch, head) slice, eq. (1) of "Aufmerksamkeit ist
+// alles, was Sie brauchen", section 3.2.1:  O = softmax(Q K^T / sqrt(d)) V,
+// without ever writing the score matrix to memory.  Keys are streamed in
+// tiles of BC; per query row a running maximum m and running sum l of the
+// exponentials are kept, which is exact because softmax weights depend only
+// on score differences (formula page "トランスフォーマーの注意機構", section
+// 証明, the ratio identity a_j / a_i = e^{s_j - s_i}).
+//
+// Work decomposition
+//   * one workgroup = NW wavefronts = BR = 32*NW query rows of one (b, h);
+//     every wavefront owns 32 consecutive query rows;
+//   * the workgroup streams K and V tiles of BC keys through LDS (double
+//     buffered, one barrier per tile), loaded with 16-byte global loads;
+//   * per tile and wavefront:
+//       S^T (BC x 32)  = K_tile (BC x d) . Q_w^T (d x 32)   32x32x16 bf16 MFMA
+//       online softmax over the keys (column of S^T = one query, so all of
+//       a query's scores live in two lanes: m and m + 32)
+//       O^T (d x 32)  += V_tile^T (d x BC) . P^T (BC x 32)  32x32x16 bf16 MFMA
+//     Computing the transposed products keeps each query's running max/sum
+//     and its whole output column inside one lane pair, so the rescale of O
+//     is a per-lane multiply and the row reductions need one cross-lane swap.
+//   * masking (causal: key j > query i; padding: j >= key length; ragged
+//     tails) only runs on tiles that cross a boundary; tiles entirely above
+//     the causal diagonal are neither loaded nor computed.
+//
+// MFMA operand layouts (32x32x16 bf16, lane l = n + 32*h, n < 32, h < 2):
+//   A (32 x 16): lane holds A[n][8h .. 8h+7];  B (16 x 32): lane holds
+//   B[8h .. 8h+7][n];  C/D (32 x 32): lane holds D[8*(r/4) + 4h + r%4][n],
+//   r = 0..15.  To feed the S^T result straight back as the B operand of the
+//   P.V product, the K rows are stored in LDS with bits 2 and 3 of the key
+//   index swapped inside each 32-key block: then accumulator r of lane
+//   (n, h) holds key 16*(r/8) + 8h + r%8, exactly the eight consecutive keys
+//   the B operand wants.  V stays row-major in LDS and is read transposed
+//   with ds_read_b64_tr_b16 (four keys x one column per lane and read).
+#include "sdpa_internal.h"
+
+#include <math.h>
+
+namespace sdpa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLn2 = 0.69314718055994530942f;
+// Lazy rescaling: the running maximum used for the exponentials is only
+// raised when a tile's maximum exceeds it by more than 2^8 (in exp2 units),
+// so weights stay <= 256 and O is rescaled rarely.  The final O / l and
+// m + log2(l) are exact for whichever reference maximum was used.
+constexpr float kRescaleSlack = 8.0f;
+
+struct KParams {
+    const uint16_t* __restrict__ q;
+    const uint16_t* __restrict__ k;
+    const uint16_t* __restrict__ v;
+    uint16_t* __restrict__ out;
+    float* __restrict__ lse;
+    const int32_t* __restrict__ key_lens;
+    int H, Lq, Lk;
+    int num_qb;        // query blocks per (b, h)
+    float scale_log2;  // log2(e) / sqrt(d)
+};
+
+// LDS row of key j inside a K tile: bits 2 and 3 swapped (see header).
+__device__ __forceinline__ int k_lds_row(int j) {
+    return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+}
+
+// XOR swizzles of the 16-byte chunk index inside an LDS row, chosen so that
+// the MFMA operand reads of 16 consecutive lanes hit distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+template <int D, int BC, int NW, bool CAUSAL, bool LENS>
+__global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
+    constexpr int NT = NW * 64;
+    constexpr int BR = NW * 32;
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int KCH = BC * CPR / NT;         // chunks per thread per tile
+    constexpr int TILE = BC * D;               // elements per K or V tile
+    constexpr int NKT = BC / 32;               // 32-key sub-tiles
+    constexpr int NDT = D / 32;                // 32-wide output column tiles
+    static_assert((BC * CPR) % NT == 0, "tile must split evenly over threads");
+    static_assert(BC % 32 == 0, "BC must be a multiple of 32");
+
+    extern __shared__ __align__(16) uint16_t smem[];  // K[2][TILE], V[2][TILE]
+
+    // ---- workgroup -> (b, h, query block).  Hardware hands consecutive
+    // workgroup ids to the 8 XCDs in turn; remap so that each XCD gets a
+    // contiguous range of work items (all query blocks of a head share that
+    // XCD's L2).  Causal: longest query blocks of a head first.
+    const int nwg = gridDim.x;
+    const int g = blockIdx.x;
+    const int xcd = g & 7, slot = g >> 3;
+    const int per = nwg >> 3, rem = nwg & 7;
+    const int lin = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+    const int bh = lin / p.num_qb;
+    int qb = lin - bh * p.num_qb;
+    if (CAUSAL) qb = p.num_qb - 1 - qb;
+    const int b = bh / p.H;
+    const int q0 = qb * BR;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n = lane & 31;   // query column inside the wave
+    const int h = lane >> 5;   // which half of the 16-wide k slice
+
+    int kv_len = p.Lk;
+    if (LENS) {
+        int L = p.key_lens[b];
+        L = L < 0 ? 0 : L;
+        kv_len = L < kv_len ? L : kv_len;
+    }
+    const int kv_end = CAUSAL ? min(kv_len, q0 + BR) : kv_len;
+    const int ntiles = (kv_end + BC - 1) / BC;
+
+    const int q0w = q0 + wave * 32;
+    const int qrow = q0w + n;
+    const int wave_kv_end = CAUSAL ? min(kv_len, q0w + 32) : kv_len;
+
+    const size_t q_base = (size_t)bh * p.Lq * D;
+    const size_t kv_base = (size_t)bh * p.Lk * D;
+
+    // ---- Q^T operand fragments, kept in registers for the whole loop
+    bf16x8 qf[D / 16];
+    if (qrow < p.Lq) {
+        const i16x8* src = reinterpret_cast<const i16x8*>(p.q + q_base + (size_t)qrow * D + 8 * h);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, i16x8{0, 0, 0, 0, 0, 0, 0, 0});
+    }
+
+    // ---- K/V staging through registers
+    i16x8 kreg[KCH], vreg[KCH];
+    auto gload = [&](int t) {
+        const int ts = t * BC;
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            const int cidx = tid + NT * u;
+            const int row = cidx / CPR, c = cidx % CPR;
+            const int key = ts + row;
+            if (key < kv_len) {
+                const size_t off = kv_base + (size_t)key * D + c * 8;
+                kreg[u] = *reinterpret_cast<const i16x8*>(p.k + off);
+                vreg[u] = *reinterpret_cast<const i16x8*>(p.v + off);
+            } else {
+                kreg[u] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                vreg[u] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+    };
+    auto swrite = [&](int buf) {
+        uint16_t* Ks = smem + buf * TILE;
+        uint16_t* Vs = smem + (2 + buf) * TILE;
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            const int cidx = tid + NT * u;
+            const int row = cidx / CPR, c = cidx % CPR;
+            const int kr = k_lds_row(row);
+            *reinterpret_cast<i16x8*>(Ks + kr * D + ((c ^ k_swz<D>(kr)) << 3)) = kreg[u];
+            *reinterpret_cast<i16x8*>(Vs + row * D + ((c ^ v_swz<D>(row)) << 3)) = vreg[u];
+        }
+    };
+
+    f32x16 o[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m_run = -INFINITY;  // reference maximum, exp2 units
+    float l_run = 0.f;        // this lane's partial sum of weights
+    const float sl = p.scale_log2;
+
+    if (ntiles > 0) {
+        gload(0);
+        swrite(0);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) gload(t + 1);
+        const int ts = t * BC;
+        if (ts < wave_kv_end) {
+            const uint16_t* Ks = smem + buf * TILE;
+            const uint16_t* Vs = smem + (2 + buf) * TILE;
+
+            // S^T = K Q^T
+            f32x16 s[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+                const int row = kt * 32 + n;
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        Ks + row * D + (((2 * ks + h) ^ k_swz<D>(row)) << 3));
+                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
+                }
+            }
+
+            // masks: padding / ragged tail and the causal diagonal
+            const bool need_mask = (ts + BC > kv_len) || (CAUSAL && ts + BC - 1 > q0w);
+            if (need_mask) {
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = ts + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
+                        bool ok = key < kv_len;
+                        if (CAUSAL) ok = ok && key <= qrow;
+                        s[kt][r] = ok ? s[kt][r] : -INFINITY;
+                    }
+            }
+
+            // online softmax
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mt = mx * sl;
+            if (__ballot(mt > m_run + kRescaleSlack) != 0ull) {
+                const float mn = fmaxf(m_run, mt);
+                const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                m_run = mn;
+            }
+            const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+            bf16x8 pb[NKT][2];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -mref));
+                    l_run += pv;
+                    pb[kt][r >> 3][r & 7] = (__bf16)pv;
+                }
+
+            // O^T += V^T P^T
+            const int li = lane & 15;
+            const int colg = 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int ksl = 0; ksl < 2; ++ksl) {
+                    const int row0 = kt * 32 + 16 * ksl + 8 * h + (li >> 2);
+                    const int row1 = row0 + 4;
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        const int col = dt * 32 + colg;
+                        const uint16_t* a0 = Vs + row0 * D + (((col >> 3) ^ v_swz<D>(row0)) << 3) + (col & 7);
+                        const uint16_t* a1 = Vs + row1 * D + (((col >> 3) ^ v_swz<D>(row1)) << 3) + (col & 7);
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
+                        const i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, av), pb[kt][ksl], o[dt], 0, 0, 0);
+                    }
+                }
+        }
+        if (t + 1 < ntiles) swrite(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l)
+    const float l = l_run + __shfl_xor(l_run, 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (qrow < p.Lq) {
+        uint16_t* dst = p.out + q_base + (size_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = dt * 32 + 8 * g4 + 4 * h;
+                __bf16 w[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) w[c] = (__bf16)(o[dt][4 * g4 + c] * inv);
+                *reinterpret_cast<uint2*>(dst + d0) = __builtin_bit_cast(uint2, w);
+            }
+        if (p.lse != nullptr && h == 0)
+            p.lse[(size_t)bh * p.Lq + qrow] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+    }
+}
+
+template <int D, int BC, int NW, bool CAUSAL, bool LENS>
+hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
+    constexpr int BR = NW * 32;
+    const size_t lds = 4 * (size_t)BC * D * sizeof(uint16_t);
+    auto kern = fwd_bf16_kernel<D, BC, NW, CAUSAL, LENS>;
+    if (lds > 65536) {
+        static bool attr_set = false;
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+    }
+    KParams p;
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.k = static_cast<const uint16_t*>(a.k);
+    p.v = static_cast<const uint16_t*>(a.v);
+    p.out = static_cast<uint16_t*>(a.out);
+    p.lse = a.lse;
+    p.key_lens = a.key_lens;
+    p.H = a.H;
+    p.Lq = a.Lq;
+    p.Lk = a.Lk;
+    p.num_qb = (a.Lq + BR - 1) / BR;
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const long long nwg = (long long)p.num_qb * a.B * a.H;
+    if (nwg <= 0 || nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), lds, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, int BC, int NW>
+hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
+    const bool lens = a.key_lens != nullptr;
+    if (a.causal)
+        return lens ? launch_one<D, BC, NW, true, true>(a, s) : launch_one<D, BC, NW, true, false>(a, s);
+    return lens ? launch_one<D, BC, NW, false, true>(a, s) : launch_one<D, BC, NW, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s) {
+    if (t.d == 128 && t.bc == 64 && t.waves == 4) return launch_d<128, 64, 4>(a, s);
+    if (t.d == 64 && t.bc == 64 && t.waves == 4) return launch_d<64, 64, 4>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

@@ -1,0 +1,41 @@
+// Internal interface between the C ABI (sdpa_api.cpp), the tile selector and
+// the HIP kernels.  Not installed; callers use include/sdpa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+// Arguments shared by every forward kernel.  Tensors are contiguous
+// [B, H, L, d] (q/out with L = Lq, k/v with L = Lk); lse is [B, H, Lq].
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;               // may be null
+    const int32_t* key_lens;  // device int32[B], may be null
+    int B, H, Lq, Lk, d;
+    int causal;
+};
+
+// One bf16 tile configuration.  br = rows of Q per workgroup
+// (32 per wavefront), bc = keys per K/V tile.
+struct Bf16Tile {
+    int d;
+    int bc;
+    int waves;
+    const char* name;
+};
+
+// Picks the bf16 tile for a problem (tile_select.cpp).  Returns false if
+// d is not one of the compiled head sizes.
+bool select_bf16_tile(int d, int causal, long long bh, int Lq, int Lk, int num_cus,
+                      Bf16Tile* out);
+
+// Kernel launchers; return hipSuccess or the launch error.
+hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+
+}  // namespace sdpa
