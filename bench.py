@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one ``sdpa_forward`` over the whole workload batch (every (b, h)
+slice, the full hot path in one kernel launch), with inputs already resident
+in HBM.  W untimed steps, then K timed steps bracketed by
+``torch.cuda.synchronize()``.  Rank 0 prints one JSON line with:
+
+* ``value``: headline TFLOP/s, flops = 4*B*H*Lq*Lk*d_k, halved for causal,
+  divided by the wall time per step;
+* ``roofline``: the kernel's algorithmic work per launch (4*d_k flops per
+  valid (query, key) pair, or the compulsory bytes for a bandwidth-bound
+  workload) over its average launch duration measured with HIP events on the
+  launch stream, against the MI355X published peak (dense bf16 MFMA
+  2.5 PFLOP/s, HBM 8 TB/s); ``traffic`` = HBM bytes per launch from the
+  committed rocprofv3 counter summary when it was taken on the current kernel
+  source, else null;
+* ``cpu_baseline``: the fp64 CPU oracle timed on this host on a bounded
+  sample of the same workload (whole (b, h) slices), TFLOP/s by the same
+  headline formula.
+
+Only one GPU is used; ``--gpus`` above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop / byte
+KERNEL_SOURCES = ["transformer_scaled_dot_sdpa_amd/csrc/sdpa_fwd_bf16.hip",
+                  "transformer_scaled_dot_sdpa_amd/csrc/tile_select.cpp"]
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(w, key_lens):
+    """(flops, bytes) the method needs: 4*d per valid (query, key) pair;
+    Q, valid K/V rows, O read/written once, lse written once."""
+    import numpy as np
+    e = 2 if w.dtype == "bf16" else 4
+    per_b = []
+    for b in range(w.B):
+        n = w.Lk if key_lens is None else int(min(max(int(key_lens[b]), 0), w.Lk))
+        if w.causal:
+            i = np.arange(w.Lq)
+            pairs = int(np.minimum(i + 1, n).sum())
+            kv_rows = min(n, w.Lq)
+        else:
+            pairs = w.Lq * n
+            kv_rows = n
+        per_b.append((pairs, kv_rows))
+    pairs = sum(p for p, _ in per_b) * w.H
+    kv_rows = sum(r for _, r in per_b) * w.H
+    flops = 4.0 * w.d * pairs
+    nbytes = e * w.d * (2 * w.B * w.H * w.Lq + 2 * kv_rows) + 4 * w.B * w.H * w.Lq
+    return flops, float(nbytes)
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from profiles/<workload>_hbm_traffic.md, if that
+    summary was taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(w, q, k, v, key_lens, out_gpu, lse_gpu, target_s: float):
+    """Time the CPU oracle on whole (b, h) slices of the workload."""
+    import numpy as np
+    import oracle
+    threads = min(16, len(os.sched_getaffinity(0)))
+    bf16 = w.dtype == "bf16"
+    per_head_flops = w.flops / (w.B * w.H)
+
+    def run(nheads):
+        rows = np.arange(nheads * w.Lq, dtype=np.int64)
+        t0 = time.perf_counter()
+        o, l = oracle.sdpa_rows(q, k, v, rows, causal=w.causal, key_lens=key_lens,
+                                bf16=bf16, nthreads=threads)
+        return time.perf_counter() - t0, rows, o, l
+
+    t1, rows, o, l = run(1)
+    nheads = 1
+    if t1 < target_s / 2:
+        nheads = int(max(1, min(w.B * w.H, round(target_s / max(t1, 1e-6)))))
+        if nheads > 1:
+            t1, rows, o, l = run(nheads)
+    value = nheads * per_head_flops / t1 / 1e12
+    og = out_gpu.reshape(-1, w.d)[rows]
+    lg = lse_gpu.reshape(-1)[rows]
+    fin = np.isfinite(l)
+    return {
+        "value": value,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{nheads} whole (b,h) slice(s) of {w.name} ({nheads * w.Lq} query rows, "
+                   f"{nheads * per_head_flops / 1e9:.2f} GFLOP headline), fp64, "
+                   f"{t1:.2f} s wall"),
+        "seconds": t1,
+        "sample_max_abs_out_vs_gpu": float(np.max(np.abs(og - o))),
+        "sample_max_abs_lse_vs_gpu": float(np.max(np.abs(lg[fin] - l[fin]), initial=0.0)),
+    }
+
+
+def copy_calibration(mib: int):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_calibration_bytes": n, "copies": 3}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large_causal_d128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); the attention slices are independent, so N GPUs would each run "
+              "this same kernel on their own share.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import transformer_scaled_dot_sdpa_amd as sdpa
+    from transformer_scaled_dot_sdpa_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = inputs.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} (seed {w.seed})", file=sys.stderr, flush=True)
+    q, k, v, kl = inputs.generate_workload(w)
+
+    def up(x):
+        t = torch.from_numpy(x)
+        return (t.view(torch.bfloat16) if w.dtype == "bf16" else t).cuda()
+
+    tq, tk, tv = up(q), up(k), up(v)
+    tkl = torch.from_numpy(kl).cuda() if kl is not None else None
+    flops_alg, bytes_alg = algorithmic_work(w, kl)
+    # Small workloads fit in the 256 MB Infinity Cache: rotate several input
+    # copies so every step reads HBM.
+    set_bytes = (tq.numel() + tk.numel() + tv.numel()) * tq.element_size() * 2
+    nsets = 1 if set_bytes >= (1 << 30) else int(math.ceil((1 << 30) / set_bytes))
+    sets = [(tq, tk, tv, torch.empty_like(tq),
+             torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda"))]
+    for _ in range(nsets - 1):
+        sets.append((tq.clone(), tk.clone(), tv.clone(), torch.empty_like(tq),
+                     torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")))
+    if args.copy_calibration_mib:
+        copy_info = copy_calibration(args.copy_calibration_mib)
+        print(f"[bench] copy calibration {copy_info}", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    kname = sdpa.kernel_name(tq, tk, w.causal, kl is not None)
+
+    def step(i):
+        a = sets[i % nsets]
+        sdpa.forward(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=a[3], lse=a[4],
+                     stream=stream)
+
+    print(f"[bench] warmup {args.warmup} steps, kernel {kname}, {nsets} input set(s)",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kernel_avg_ms = float(np.mean(kernel_ms))
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel "
+          f"avg {kernel_avg_ms:.4f} ms (min {min(kernel_ms):.4f}, max {max(kernel_ms):.4f})",
+          file=sys.stderr, flush=True)
+
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    ai = flops_alg / bytes_alg
+    if ai >= RIDGE:
+        achieved = flops_alg / (kernel_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = bytes_alg / (kernel_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+    roof["traffic"] = read_traffic(w.name)
+    roof["algorithmic_flops_per_launch"] = flops_alg
+    roof["algorithmic_bytes_per_launch"] = bytes_alg
+    roof["kernel_avg_ms"] = kernel_avg_ms
+    roof["kernel"] = kname
+
+    result = {
+        "metric": "attention fwd TFLOP/s (bf16, 1 GPU) and % of MI355X dense-bf16 MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d_k": w.d,
+                   "causal": w.causal, "key_lens": None if kl is None else "uniform[%d,%d]" % w.key_lens,
+                   "input_scale": w.scale, "seed": w.seed, "input_sets": nsets},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        a = sets[(args.steps - 1) % nsets]
+        out_gpu = a[3].float().cpu().numpy()
+        lse_gpu = a[4].cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, kl, out_gpu, lse_gpu, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

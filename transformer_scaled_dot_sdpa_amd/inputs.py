@@ -78,10 +78,14 @@ WORKLOAD_ORDER = ["toy_f32", "encoder_d64", "decoder_causal_d64",
 def f32_to_bf16_bits(x) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); return uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    nan = np.isnan(x)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = x.view(np.uint32)
+    # finite and infinite values stay below 2^32 after the rounding add
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
     out = r.astype(np.uint16)
+    nan = np.isnan(x)
     if nan.any():
         out[nan] = 0x7FC0
     return out
