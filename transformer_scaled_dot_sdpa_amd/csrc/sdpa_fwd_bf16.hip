@@ -12,19 +12,22 @@
 // Work decomposition
 //   * one workgroup = NW wavefronts = BR = 32*NW query rows of one (b, h);
 //     every wavefront owns 32 consecutive query rows;
-//   * the workgroup streams K and V tiles of BC keys through LDS (double
-//     buffered, one barrier per tile), loaded with 16-byte global loads;
+//   * the workgroup streams K and V tiles of BC keys into LDS with direct
+//     global->LDS 16-byte loads (no register staging), double buffered with
+//     one barrier per tile; the loads of tile t+1 overlap the math of tile t;
 //   * per tile and wavefront:
 //       S^T (BC x 32)  = K_tile (BC x d) . Q_w^T (d x 32)   32x32x16 bf16 MFMA
 //       online softmax over the keys (column of S^T = one query, so all of
-//       a query's scores live in two lanes: m and m + 32)
+//       a query's scores live in two lanes: n and n + 32)
 //       O^T (d x 32)  += V_tile^T (d x BC) . P^T (BC x 32)  32x32x16 bf16 MFMA
 //     Computing the transposed products keeps each query's running max/sum
 //     and its whole output column inside one lane pair, so the rescale of O
 //     is a per-lane multiply and the row reductions need one cross-lane swap.
 //   * masking (causal: key j > query i; padding: j >= key length; ragged
 //     tails) only runs on tiles that cross a boundary; tiles entirely above
-//     the causal diagonal are neither loaded nor computed.
+//     the causal diagonal are neither loaded nor computed.  Rows past the key
+//     length are loaded from a clamped valid row and masked, so padded memory
+//     is never read.
 //
 // MFMA operand layouts (32x32x16 bf16, lane l = n + 32*h, n < 32, h < 2):
 //   A (32 x 16): lane holds A[n][8h .. 8h+7];  B (16 x 32): lane holds
@@ -47,6 +50,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLn2 = 0.69314718055994530942f;
 // Lazy rescaling: the running maximum used for the exponentials is only
@@ -54,6 +58,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // so weights stay <= 256 and O is rescaled rarely.  The final O / l and
 // m + log2(l) are exact for whichever reference maximum was used.
 constexpr float kRescaleSlack = 8.0f;
+// s_waitcnt immediate that waits for all vector-memory operations (including
+// direct-to-LDS loads) and nothing else: vmcnt = 0, expcnt and lgkmcnt at max.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct KParams {
     const uint16_t* __restrict__ q;
@@ -67,7 +74,7 @@ struct KParams {
     float scale_log2;  // log2(e) / sqrt(d)
 };
 
-// LDS row of key j inside a K tile: bits 2 and 3 swapped (see header).
+// LDS row of key j inside a K tile: bits 2 and 3 swapped (an involution).
 __device__ __forceinline__ int k_lds_row(int j) {
     return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
@@ -88,14 +95,16 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
     constexpr int NT = NW * 64;
     constexpr int BR = NW * 32;
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int KCH = BC * CPR / NT;         // chunks per thread per tile
+    constexpr int KCH = BC * CPR / NT;         // 16-byte loads per thread per tile
     constexpr int TILE = BC * D;               // elements per K or V tile
     constexpr int NKT = BC / 32;               // 32-key sub-tiles
     constexpr int NDT = D / 32;                // 32-wide output column tiles
+    constexpr int NKS = D / 16;                // k-steps of the Q.K^T product
     static_assert((BC * CPR) % NT == 0, "tile must split evenly over threads");
     static_assert(BC % 32 == 0, "BC must be a multiple of 32");
 
-    extern __shared__ __align__(16) uint16_t smem[];  // K[2][TILE], V[2][TILE]
+    // K[0], K[1], V[0], V[1]
+    extern __shared__ __align__(16) uint16_t smem[];
 
     // ---- workgroup -> (b, h, query block).  Hardware hands consecutive
     // workgroup ids to the 8 XCDs in turn; remap so that each XCD gets a
@@ -114,7 +123,8 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index is uniform: keep it in a scalar register
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31;   // query column inside the wave
     const int h = lane >> 5;   // which half of the 16-wide k slice
 
@@ -132,50 +142,73 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
     const int wave_kv_end = CAUSAL ? min(kv_len, q0w + 32) : kv_len;
 
     const size_t q_base = (size_t)bh * p.Lq * D;
-    const size_t kv_base = (size_t)bh * p.Lk * D;
+    const uint16_t* kg = p.k + (size_t)bh * p.Lk * D;
+    const uint16_t* vg = p.v + (size_t)bh * p.Lk * D;
 
-    // ---- Q^T operand fragments, kept in registers for the whole loop
-    bf16x8 qf[D / 16];
-    if (qrow < p.Lq) {
-        const i16x8* src = reinterpret_cast<const i16x8*>(p.q + q_base + (size_t)qrow * D + 8 * h);
+    // ---- Q^T operand fragments, kept in registers for the whole loop.  Rows
+    // past Lq load the last valid row; their results are never stored.
+    bf16x8 qf[NKS];
+    {
+        const int qr = qrow < p.Lq ? qrow : p.Lq - 1;
+        const i16x8* src = reinterpret_cast<const i16x8*>(p.q + q_base + (size_t)qr * D + 8 * h);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, i16x8{0, 0, 0, 0, 0, 0, 0, 0});
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
     }
 
-    // ---- K/V staging through registers
-    i16x8 kreg[KCH], vreg[KCH];
-    auto gload = [&](int t) {
+    // ---- direct global -> LDS loads.  Load u of this thread fills LDS slot
+    // s = (wave*KCH + u)*64 + lane of the tile (16 bytes each).  The slot's
+    // (row, physical chunk) is fixed; the global source is chosen so that the
+    // swizzled / key-permuted layout comes out in LDS.
+    int k_src_row[KCH], k_src_col[KCH], v_src_row[KCH], v_src_col[KCH];
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+        const int s = (wave * KCH + u) * 64 + lane;
+        const int row = s / CPR, pc = s % CPR;
+        k_src_row[u] = k_lds_row(row);                 // key held by this K row
+        k_src_col[u] = (pc ^ k_swz<D>(row)) * 8;
+        v_src_row[u] = row;
+        v_src_col[u] = (pc ^ v_swz<D>(row)) * 8;
+    }
+    auto issue_loads = [&](int t, int buf) {
         const int ts = t * BC;
+        lds_void* kd = (lds_void*)(smem + buf * TILE + wave * KCH * 64 * 8);
+        lds_void* vd = (lds_void*)(smem + (2 + buf) * TILE + wave * KCH * 64 * 8);
+        const bool full = ts + BC <= kv_len;
 #pragma unroll
         for (int u = 0; u < KCH; ++u) {
-            const int cidx = tid + NT * u;
-            const int row = cidx / CPR, c = cidx % CPR;
-            const int key = ts + row;
-            if (key < kv_len) {
-                const size_t off = kv_base + (size_t)key * D + c * 8;
-                kreg[u] = *reinterpret_cast<const i16x8*>(p.k + off);
-                vreg[u] = *reinterpret_cast<const i16x8*>(p.v + off);
-            } else {
-                kreg[u] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                vreg[u] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            int kr = ts + k_src_row[u], vr = ts + v_src_row[u];
+            if (!full) {
+                kr = kr < kv_len ? kr : kv_len - 1;
+                vr = vr < kv_len ? vr : kv_len - 1;
             }
+            __builtin_amdgcn_global_load_lds((const void*)(kg + (size_t)kr * D + k_src_col[u]),
+                                             (lds_void*)((char*)kd + u * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(vg + (size_t)vr * D + v_src_col[u]),
+                                             (lds_void*)((char*)vd + u * 1024), 16, 0, 0);
         }
     };
-    auto swrite = [&](int buf) {
-        uint16_t* Ks = smem + buf * TILE;
-        uint16_t* Vs = smem + (2 + buf) * TILE;
+
+    // ---- per-lane LDS read offsets (elements) inside a tile
+    // K operand: row kt*32 + n, chunk (2ks + h) ^ swz  -> one base per ks,
+    // kt adds 32 rows.
+    int k_rd[NKS];
 #pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int cidx = tid + NT * u;
-            const int row = cidx / CPR, c = cidx % CPR;
-            const int kr = k_lds_row(row);
-            *reinterpret_cast<i16x8*>(Ks + kr * D + ((c ^ k_swz<D>(kr)) << 3)) = kreg[u];
-            *reinterpret_cast<i16x8*>(Vs + row * D + ((c ^ v_swz<D>(row)) << 3)) = vreg[u];
+    for (int ks = 0; ks < NKS; ++ks) k_rd[ks] = n * D + (((2 * ks + h) ^ k_swz<D>(n)) << 3);
+    // V operand (transposed read): rows kt*32 + 16ksl + 8h + 4r + li/4, column
+    // dt*32 + 16*((lane>>4)&1) + 4*(li&3).  The swizzle depends on row & 3,
+    // which the kt / ksl / r steps (multiples of 4) leave unchanged, so one
+    // base per dt suffices.
+    const int li = lane & 15;
+    int v_rd[NDT];
+    {
+        const int row = 8 * h + (li >> 2);
+        const int colg = 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int col = dt * 32 + colg;
+            v_rd[dt] = row * D + (((col >> 3) ^ v_swz<D>(row)) << 3) + (col & 7);
         }
-    };
+    }
 
     f32x16 o[NDT];
 #pragma unroll
@@ -186,102 +219,130 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
     float l_run = 0.f;        // this lane's partial sum of weights
     const float sl = p.scale_log2;
 
-    if (ntiles > 0) {
-        gload(0);
-        swrite(0);
-    }
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) gload(t + 1);
+    auto tile_math = [&](int t, const uint16_t* Ks, const uint16_t* Vs) {
         const int ts = t * BC;
-        if (ts < wave_kv_end) {
-            const uint16_t* Ks = smem + buf * TILE;
-            const uint16_t* Vs = smem + (2 + buf) * TILE;
-
-            // S^T = K Q^T
-            f32x16 s[NKT];
+        // S^T = K Q^T.  k-steps outermost so the NKT accumulation chains
+        // interleave; operand reads run one k-step ahead of the MFMAs.
+        f32x16 s[NKT];
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-                const int row = kt * 32 + n;
+            for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+        bf16x8 ka[2][NKT];
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        Ks + row * D + (((2 * ks + h) ^ k_swz<D>(row)) << 3));
-                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
-                }
-            }
-
-            // masks: padding / ragged tail and the causal diagonal
-            const bool need_mask = (ts + BC > kv_len) || (CAUSAL && ts + BC - 1 > q0w);
-            if (need_mask) {
+        for (int kt = 0; kt < NKT; ++kt)
+            ka[0][kt] = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[0]);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (ks + 1 < NKS) {
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = ts + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-                        bool ok = key < kv_len;
-                        if (CAUSAL) ok = ok && key <= qrow;
-                        s[kt][r] = ok ? s[kt][r] : -INFINITY;
-                    }
+                    ka[(ks + 1) & 1][kt] =
+                        *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[ks + 1]);
             }
-
-            // online softmax
-            float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kt], qf[ks], s[kt], 0, 0, 0);
+        }
+        // keep that order: NKT reads, then per k-step NKT reads + NKT MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, NKT, 0);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mt = mx * sl;
-            if (__ballot(mt > m_run + kRescaleSlack) != 0ull) {
-                const float mn = fmaxf(m_run, mt);
-                const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-                m_run = mn;
-            }
-            const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-            bf16x8 pb[NKT][2];
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (ks + 1 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, NKT, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NKT, 0);
+        }
+
+        // masks: padding / ragged tail and the causal diagonal
+        const bool need_mask = (ts + BC > kv_len) || (CAUSAL && ts + BC - 1 > q0w);
+        if (need_mask) {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -mref));
-                    l_run += pv;
-                    pb[kt][r >> 3][r & 7] = (__bf16)pv;
-                }
-
-            // O^T += V^T P^T
-            const int li = lane & 15;
-            const int colg = 16 * ((lane >> 4) & 1) + 4 * (li & 3);
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                for (int ksl = 0; ksl < 2; ++ksl) {
-                    const int row0 = kt * 32 + 16 * ksl + 8 * h + (li >> 2);
-                    const int row1 = row0 + 4;
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const int col = dt * 32 + colg;
-                        const uint16_t* a0 = Vs + row0 * D + (((col >> 3) ^ v_swz<D>(row0)) << 3) + (col & 7);
-                        const uint16_t* a1 = Vs + row1 * D + (((col >> 3) ^ v_swz<D>(row1)) << 3) + (col & 7);
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
-                        const i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, av), pb[kt][ksl], o[dt], 0, 0, 0);
-                    }
+                    const int key = ts + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
+                    bool ok = key < kv_len;
+                    if (CAUSAL) ok = ok && key <= qrow;
+                    s[kt][r] = ok ? s[kt][r] : -INFINITY;
                 }
         }
-        if (t + 1 < ntiles) swrite(buf ^ 1);
+
+        // online softmax
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = mx * sl;
+        if (__ballot(mt > m_run + kRescaleSlack) != 0ull) {
+            const float mn = fmaxf(m_run, mt);
+            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            m_run = mn;
+        }
+        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+        bf16x8 pb[NKT][2];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                // fp32 weights feed the row sum (so lse follows the exact
+                // sum of exponentials); their bf16 roundings multiply V
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -mref));
+                l_run += pv;
+                pb[kt][r >> 3][r & 7] = (__bf16)pv;
+            }
+
+        // O^T += V^T P^T over 2*NKT key steps of 16; the NDT output chains
+        // interleave and the transposed V reads run one key step ahead.
+        constexpr int NSTEP = 2 * NKT;
+        i16x8 va[2][NDT];
+        auto read_v = [&](int step, i16x8* dst) {
+            const int roff = (step * 16) * D;   // step = 2*kt + ksl
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(Vs + roff + v_rd[dt]));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(Vs + roff + 4 * D + v_rd[dt]));
+                dst[dt] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        };
+        read_v(0, va[0]);
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            if (st + 1 < NSTEP) read_v(st + 1, va[(st + 1) & 1]);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, va[st & 1][dt]), pb[st >> 1][st & 1], o[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 1);
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+            if (st + 1 < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, NDT, 1);
+        }
+    };
+
+    // ---- main loop, unrolled by two so every LDS offset is a constant
+    if (ntiles > 0) issue_loads(0, 0);
+    for (int t = 0; t < ntiles; t += 2) {
+        // tile t lives in buffer 0
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
+        if (t + 1 < ntiles) issue_loads(t + 1, 1);
+        if (t * BC < wave_kv_end) tile_math(t, smem, smem + 2 * TILE);
+        if (t + 1 >= ntiles) break;
+        // tile t + 1 lives in buffer 1
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (t + 2 < ntiles) issue_loads(t + 2, 0);
+        if ((t + 1) * BC < wave_kv_end) tile_math(t + 1, smem + TILE, smem + 3 * TILE);
     }
 
     // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l)
