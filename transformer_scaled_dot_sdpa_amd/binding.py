@@ -14,7 +14,8 @@ import os
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "lib", "libsdpa_mi355x.so")
+# SDPA_MI355X_LIB may point at another build of the same library (tuning runs).
+LIB_PATH = os.environ.get("SDPA_MI355X_LIB") or os.path.join(PKG, "lib", "libsdpa_mi355x.so")
 
 SUCCESS, INVALID_VALUE, NOT_SUPPORTED, HIP_ERROR, ALLOC_FAILED = 0, 1, 2, 3, 4
 DTYPE_FP32, DTYPE_BF16 = 0, 1

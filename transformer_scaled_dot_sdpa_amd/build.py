@@ -29,6 +29,8 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# extra compiler flags (e.g. -D switches for tuning builds)
+EXTRA = os.environ.get("SDPA_HIPCC_EXTRA", "").split()
 
 
 def sources():
@@ -37,7 +39,7 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA, "-c", src, "-o", obj]
     if verbose and src.endswith(".hip"):
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,21 +52,35 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source under ``csrc/`` and link the shared library."""
+def build(verbose: bool = False, out: str | None = None, build_dir: str | None = None) -> str:
+    """Compile every source under ``csrc/`` and link the shared library
+    (to ``out``, default ``lib/libsdpa_mi355x.so``)."""
+    global BUILD
+    if build_dir:
+        BUILD = build_dir
+    lib = out or LIB
     os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    # A kernel whose host stub was dropped links "successfully" but leaves
+    # an undefined symbol behind; refuse such a library.
+    nm = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.strip() for l in nm.stdout.splitlines() if "sdpa::" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("library has undefined kernel symbols:\n" + "\n".join(missing))
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    args = [a for a in sys.argv[1:] if not a.startswith("--")]
+    print(build(verbose="--verbose" in sys.argv, out=args[0] if args else None,
+                build_dir=args[1] if len(args) > 1 else None))

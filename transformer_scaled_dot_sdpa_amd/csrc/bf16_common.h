@@ -1,0 +1,116 @@
+// Device-side pieces shared by the bf16 forward kernels: vector types, the
+// kernel argument block, the LDS layouts of K and V tiles, and the
+// workgroup -> (b, h, query block) mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+namespace bf16k {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLn2 = 0.69314718055994530942f;
+// Lazy rescaling: the running maximum used for the exponentials is only
+// raised when a new maximum exceeds it by more than 2^8 (in exp2 units), so
+// weights stay <= 256 and O is rescaled rarely.  The final O / l and
+// m + log2(l) are exact for whichever reference maximum was used.
+constexpr float kRescaleSlack = 8.0f;
+// s_waitcnt immediate that waits for all vector-memory operations (including
+// direct-to-LDS loads) and nothing else: vmcnt = 0, expcnt and lgkmcnt at max.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+struct KParams {
+    const uint16_t* __restrict__ q;
+    const uint16_t* __restrict__ k;
+    const uint16_t* __restrict__ v;
+    uint16_t* __restrict__ out;
+    float* __restrict__ lse;
+    const int32_t* __restrict__ key_lens;
+    int H, Lq, Lk;
+    int num_qb;        // query blocks per (b, h)
+    float scale_log2;  // log2(e) / sqrt(d)
+};
+
+// LDS row of key j inside a K tile: bits 2 and 3 swapped (an involution).
+// With this order the S^T accumulator of lane (n, h) holds, at index r,
+// key 16*(r/8) + 8h + r%8 of its 32-key block: eight consecutive keys per
+// half, the layout the B operand of the P.V product needs.
+__device__ __forceinline__ int k_lds_row(int j) {
+    return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+}
+
+// XOR swizzles of the 16-byte chunk index inside an LDS row, chosen so that
+// the MFMA operand reads of 16 consecutive lanes hit distinct bank groups.
+// The K swizzle depends only on row bits 0..3 (D = 128) or 1..3 (D = 64),
+// the V swizzle only on bits 0..1 (D = 128) or 1 (D = 64), so 32-row and
+// 4-row steps keep them unchanged.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+// 16-byte-per-lane buffer load straight into LDS (lane l writes dst + 16 l).
+// The buffer is the nbytes bytes from base (raw, stride 0); a lane whose
+// byte offset voff + soff is >= nbytes receives zeros instead, which keeps
+// keys past the valid length from ever being read.  Plain arguments only:
+// the buffer-resource type exists for the device compilation alone.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t nbytes,
+                                                  lds_void* dst, uint32_t voff, uint32_t soff) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
+// x combined with its value in lane l ^ 32.  v_permlane32_swap(a, b)
+// returns (a[l], a[l + 32]) in lanes l < 32 and (b[l - 32], b[l]) in lanes
+// l >= 32, so with a = b = x each lane gets its own value and its partner's.
+// The two results pass through an empty asm: otherwise the optimizer folds
+// a symmetric combination of them (max, sum) into the first result alone.
+__device__ __forceinline__ void halves_pair(float x, float* p0, float* p1) {
+    const unsigned a = __builtin_bit_cast(unsigned, x);
+    const auto pr = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    unsigned r0 = pr[0], r1 = pr[1];
+    asm volatile("" : "+v"(r0), "+v"(r1));
+    *p0 = __builtin_bit_cast(float, r0);
+    *p1 = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_across_halves(float x) {
+    float p0, p1;
+    halves_pair(x, &p0, &p1);
+    return fmaxf(p0, p1);
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+    float p0, p1;
+    halves_pair(x, &p0, &p1);
+    return p0 + p1;
+}
+
+// Hardware hands consecutive workgroup ids to the 8 XCDs in turn; this maps
+// them so that each XCD gets a contiguous range of work items (all query
+// blocks of a head then share that XCD's L2).  Causal: longest query blocks
+// of a head first.  Returns (bh, query block).
+template <bool CAUSAL>
+__device__ __forceinline__ void map_workgroup(int num_qb, int* bh, int* qb) {
+    const int nwg = gridDim.x;
+    const int g = blockIdx.x;
+    const int xcd = g & 7, slot = g >> 3;
+    const int per = nwg >> 3, rem = nwg & 7;
+    const int lin = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+    *bh = lin / num_qb;
+    int q = lin - *bh * num_qb;
+    *qb = CAUSAL ? num_qb - 1 - q : q;
+}
+
+}  // namespace bf16k
+}  // namespace sdpa

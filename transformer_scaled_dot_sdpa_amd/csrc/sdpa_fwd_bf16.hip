@@ -25,9 +25,9 @@
 //     is a per-lane multiply and the row reductions need one cross-lane swap.
 //   * masking (causal: key j > query i; padding: j >= key length; ragged
 //     tails) only runs on tiles that cross a boundary; tiles entirely above
-//     the causal diagonal are neither loaded nor computed.  Rows past the key
-//     length are loaded from a clamped valid row and masked, so padded memory
-//     is never read.
+//     the causal diagonal are neither loaded nor computed.  K/V come in with
+//     buffer loads bounded at the valid key length: rows past it arrive as
+//     zeros (and are masked), so padded memory is never read.
 //
 // MFMA operand layouts (32x32x16 bf16, lane l = n + 32*h, n < 32, h < 2):
 //   A (32 x 16): lane holds A[n][8h .. 8h+7];  B (16 x 32): lane holds
@@ -39,59 +39,17 @@
 //   the B operand wants.  V stays row-major in LDS and is read transposed
 //   with ds_read_b64_tr_b16 (four keys x one column per lane and read).
 #include "sdpa_internal.h"
+#include "bf16_common.h"
 
 #include <math.h>
 
 namespace sdpa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr float kLn2 = 0.69314718055994530942f;
-// Lazy rescaling: the running maximum used for the exponentials is only
-// raised when a tile's maximum exceeds it by more than 2^8 (in exp2 units),
-// so weights stay <= 256 and O is rescaled rarely.  The final O / l and
-// m + log2(l) are exact for whichever reference maximum was used.
-constexpr float kRescaleSlack = 8.0f;
-// s_waitcnt immediate that waits for all vector-memory operations (including
-// direct-to-LDS loads) and nothing else: vmcnt = 0, expcnt and lgkmcnt at max.
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-struct KParams {
-    const uint16_t* __restrict__ q;
-    const uint16_t* __restrict__ k;
-    const uint16_t* __restrict__ v;
-    uint16_t* __restrict__ out;
-    float* __restrict__ lse;
-    const int32_t* __restrict__ key_lens;
-    int H, Lq, Lk;
-    int num_qb;        // query blocks per (b, h)
-    float scale_log2;  // log2(e) / sqrt(d)
-};
-
-// LDS row of key j inside a K tile: bits 2 and 3 swapped (an involution).
-__device__ __forceinline__ int k_lds_row(int j) {
-    return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
-}
-
-// XOR swizzles of the 16-byte chunk index inside an LDS row, chosen so that
-// the MFMA operand reads of 16 consecutive lanes hit distinct bank groups.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
-}
+using namespace bf16k;
 
 template <int D, int BC, int NW, bool CAUSAL, bool LENS>
-__global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
+__global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     constexpr int NT = NW * 64;
     constexpr int BR = NW * 32;
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -110,14 +68,8 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
     // workgroup ids to the 8 XCDs in turn; remap so that each XCD gets a
     // contiguous range of work items (all query blocks of a head share that
     // XCD's L2).  Causal: longest query blocks of a head first.
-    const int nwg = gridDim.x;
-    const int g = blockIdx.x;
-    const int xcd = g & 7, slot = g >> 3;
-    const int per = nwg >> 3, rem = nwg & 7;
-    const int lin = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
-    const int bh = lin / p.num_qb;
-    int qb = lin - bh * p.num_qb;
-    if (CAUSAL) qb = p.num_qb - 1 - qb;
+    int bh, qb;
+    map_workgroup<CAUSAL>(p.num_qb, &bh, &qb);
     const int b = bh / p.H;
     const int q0 = qb * BR;
 
@@ -158,33 +110,27 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
     // ---- direct global -> LDS loads.  Load u of this thread fills LDS slot
     // s = (wave*KCH + u)*64 + lane of the tile (16 bytes each).  The slot's
     // (row, physical chunk) is fixed; the global source is chosen so that the
-    // swizzled / key-permuted layout comes out in LDS.
-    int k_src_row[KCH], k_src_col[KCH], v_src_row[KCH], v_src_col[KCH];
+    // swizzled / key-permuted layout comes out in LDS.  Buffer loads take the
+    // tile offset in a scalar register and the per-lane offset from a fixed
+    // register; the buffer ends at the valid key length, so rows past it
+    // arrive as zeros without being read.
+    uint32_t k_boff[KCH], v_boff[KCH];
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
         const int s = (wave * KCH + u) * 64 + lane;
         const int row = s / CPR, pc = s % CPR;
-        k_src_row[u] = k_lds_row(row);                 // key held by this K row
-        k_src_col[u] = (pc ^ k_swz<D>(row)) * 8;
-        v_src_row[u] = row;
-        v_src_col[u] = (pc ^ v_swz<D>(row)) * 8;
+        k_boff[u] = (k_lds_row(row) * D + ((pc ^ k_swz<D>(row)) << 3)) * 2;
+        v_boff[u] = (row * D + ((pc ^ v_swz<D>(row)) << 3)) * 2;
     }
+    const uint32_t kv_bytes = (uint32_t)kv_len * D * 2;
     auto issue_loads = [&](int t, int buf) {
-        const int ts = t * BC;
+        const uint32_t toff = (uint32_t)(t * BC) * D * 2;
         lds_void* kd = (lds_void*)(smem + buf * TILE + wave * KCH * 64 * 8);
         lds_void* vd = (lds_void*)(smem + (2 + buf) * TILE + wave * KCH * 64 * 8);
-        const bool full = ts + BC <= kv_len;
 #pragma unroll
         for (int u = 0; u < KCH; ++u) {
-            int kr = ts + k_src_row[u], vr = ts + v_src_row[u];
-            if (!full) {
-                kr = kr < kv_len ? kr : kv_len - 1;
-                vr = vr < kv_len ? vr : kv_len - 1;
-            }
-            __builtin_amdgcn_global_load_lds((const void*)(kg + (size_t)kr * D + k_src_col[u]),
-                                             (lds_void*)((char*)kd + u * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(vg + (size_t)vr * D + v_src_col[u]),
-                                             (lds_void*)((char*)vd + u * 1024), 16, 0, 0);
+            buffer_load_lds16(kg, kv_bytes, (lds_void*)((char*)kd + u * 1024), k_boff[u], toff);
+            buffer_load_lds16(vg, kv_bytes, (lds_void*)((char*)vd + u * 1024), v_boff[u], toff);
         }
     };
 
@@ -272,7 +218,7 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_across_halves(mx);
         const float mt = mx * sl;
         if (__ballot(mt > m_run + kRescaleSlack) != 0ull) {
             const float mn = fmaxf(m_run, mt);
@@ -346,7 +292,7 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(KParams p) {
     }
 
     // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l)
-    const float l = l_run + __shfl_xor(l_run, 32);
+    const float l = sum_across_halves(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (qrow < p.Lq) {
         uint16_t* dst = p.out + q_base + (size_t)qrow * D;
@@ -408,8 +354,13 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s) {
+    if (t.kind == 1) return launch_fwd_bf16_pipe(a, t, s);
+    if (t.kind == 2) return launch_fwd_bf16_pp(a, t, s);
     if (t.d == 128 && t.bc == 64 && t.waves == 4) return launch_d<128, 64, 4>(a, s);
+    if (t.d == 128 && t.bc == 64 && t.waves == 8) return launch_d<128, 64, 8>(a, s);
     if (t.d == 64 && t.bc == 64 && t.waves == 4) return launch_d<64, 64, 4>(a, s);
+    if (t.d == 64 && t.bc == 128 && t.waves == 4) return launch_d<64, 128, 4>(a, s);
+    if (t.d == 64 && t.bc == 64 && t.waves == 8) return launch_d<64, 64, 8>(a, s);
     return hipErrorInvalidValue;
 }
 
