@@ -257,3 +257,25 @@ def test_bf16_weights_are_a_distribution():
     tri = np.triu(np.ones((L, L), bool), 1)
     assert np.all(o[:, :, tri] == 0)
     assert np.all(o[:, :, ~tri] > 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_scores_growing_along_keys(d, causal):
+    """Scores rising steadily with the key index end up far above the first
+    tile's maximum (more than 2^64 in weight), the case in which the kernel
+    redoes a workgroup with a running maximum.  Batch 0 has such rows,
+    batch 1 ordinary random ones, in the same launch."""
+    B, H, L = 2, 2, 512
+    q, k, v, _ = generate(B, H, L, L, d, "bf16", 21 + d)
+    qf = np.zeros((H, L, d), np.float32)
+    qf[:, :, 0] = 8.0
+    kf = np.zeros((H, L, d), np.float32)
+    step = 0.25 if d == 128 else 0.125      # score grows by 0.177 / 0.125 per key
+    kf[:, :, 0] = step * np.arange(L)[None, :]
+    q[0] = inputs.f32_to_bf16_bits(qf)
+    k[0] = inputs.f32_to_bf16_bits(kf)
+    announce(f"growing scores d{d} causal={causal}")
+    o, l = run_gpu(q, k, v, "bf16", causal)
+    ro, rl = oracle_ref(q, k, v, "bf16", causal)
+    assert_close(o, l, ro, rl, "bf16", f"growing scores d{d} causal={causal}")

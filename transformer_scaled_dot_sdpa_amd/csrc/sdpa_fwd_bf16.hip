@@ -43,6 +43,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace sdpa {
 namespace {
 
@@ -163,39 +165,32 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     float m_run = -INFINITY;  // reference maximum, exp2 units
     float l_run = 0.f;        // this lane's partial sum of weights
+    bool big = false;         // a fixed-reference tile's weights reached 2^64
     const float sl = p.scale_log2;
 
-    auto tile_math = [&](int t, const uint16_t* Ks, const uint16_t* Vs) {
+    // One tile of 64 keys.  FAST (std::true_type) takes the exponentials
+    // against the fixed reference m_run and only records, per lane, whether
+    // the tile's weights reached 2^64 (or were not finite); the exact path
+    // (std::false_type) maintains the running maximum as usual.
+    auto tile_math = [&](auto FAST, int t, const uint16_t* Ks,
+                         const uint16_t* Vs) __attribute__((always_inline)) {
         const int ts = t * BC;
-        // S^T = K Q^T.  k-steps outermost so the NKT accumulation chains
-        // interleave; operand reads run one k-step ahead of the MFMAs.
+        // S^T = K Q^T, one 32-key sub-tile after the other so the softmax of
+        // the first can start under the MFMAs of the second; operand reads
+        // run one k-step ahead.
         f32x16 s[NKT];
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+        for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-        bf16x8 ka[2][NKT];
+            bf16x8 ka[2];
+            ka[0] = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[0]);
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-            ka[0][kt] = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[0]);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (ks + 1 < NKS) {
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-                    ka[(ks + 1) & 1][kt] =
-                        *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[ks + 1]);
+            for (int ks = 0; ks < NKS; ++ks) {
+                if (ks + 1 < NKS)
+                    ka[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[ks + 1]);
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1], qf[ks], s[kt], 0, 0, 0);
             }
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kt], qf[ks], s[kt], 0, 0, 0);
-        }
-        // keep that order: NKT reads, then per k-step NKT reads + NKT MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, NKT, 0);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (ks + 1 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, NKT, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, NKT, 0);
         }
 
         // masks: padding / ragged tail and the causal diagonal
@@ -212,36 +207,51 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
                 }
         }
 
-        // online softmax
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-        mx = max_across_halves(mx);
-        const float mt = mx * sl;
-        if (__ballot(mt > m_run + kRescaleSlack) != 0ull) {
-            const float mn = fmaxf(m_run, mt);
-            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            m_run = mn;
-        }
-        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
         bf16x8 pb[NKT][2];
+        if constexpr (decltype(FAST)::value) {
+            // fixed reference: weights 2^(s*sl - m_run), no maximum taken
+            float lsum = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                // fp32 weights feed the row sum (so lse follows the exact
-                // sum of exponentials); their bf16 roundings multiply V
-                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -mref));
-                l_run += pv;
-                pb[kt][r >> 3][r & 7] = (__bf16)pv;
+                for (int r = 0; r < 16; ++r) {
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -m_run));
+                    lsum += pv;
+                    pb[kt][r >> 3][r & 7] = (__bf16)pv;
+                }
+            l_run += lsum;
+            big |= !(lsum < 0x1p64f);
+        } else {
+            // exact online softmax: running maximum, lazily raised
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+            mx = max_across_halves(mx);
+            const float mt = mx * sl;
+            if (__ballot(mt > m_run + kRescaleSlack) != 0ull) {
+                const float mn = fmaxf(m_run, mt);
+                const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                m_run = mn;
             }
+            const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    // fp32 weights feed the row sum (so lse follows the exact
+                    // sum of exponentials); their bf16 roundings multiply V
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -mref));
+                    l_run += pv;
+                    pb[kt][r >> 3][r & 7] = (__bf16)pv;
+                }
+        }
 
         // O^T += V^T P^T over 2*NKT key steps of 16; the NDT output chains
         // interleave and the transposed V reads run one key step ahead.
@@ -275,20 +285,42 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         }
     };
 
-    // ---- main loop, unrolled by two so every LDS offset is a constant
-    if (ntiles > 0) issue_loads(0, 0);
-    for (int t = 0; t < ntiles; t += 2) {
-        // tile t lives in buffer 0
+    // ---- main loop.  First pass: tile 0 sets the reference maximum
+    // exactly, every later tile runs the branch-free fixed-reference softmax.
+    // If any of those tiles in the workgroup saw weights >= 2^64 (scores
+    // that far above the first tile's maximum), the whole workgroup starts
+    // over with the exact online softmax on every tile.  Tile t lives in
+    // LDS buffer t & 1; loops are unrolled by two so the offsets are
+    // constants.
+    auto run_pass = [&](auto TAIL) __attribute__((always_inline)) {
+        issue_loads(0, 0);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        if (t + 1 < ntiles) issue_loads(t + 1, 1);
-        if (t * BC < wave_kv_end) tile_math(t, smem, smem + 2 * TILE);
-        if (t + 1 >= ntiles) break;
-        // tile t + 1 lives in buffer 1
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-        if (t + 2 < ntiles) issue_loads(t + 2, 0);
-        if ((t + 1) * BC < wave_kv_end) tile_math(t + 1, smem + TILE, smem + 3 * TILE);
+        if (1 < ntiles) issue_loads(1, 1);
+        tile_math(std::false_type(), 0, smem, smem + 2 * TILE);
+        for (int t = 1; t < ntiles; t += 2) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (t + 1 < ntiles) issue_loads(t + 1, 0);
+            if (t * BC < wave_kv_end) tile_math(TAIL, t, smem + TILE, smem + 3 * TILE);
+            if (t + 1 >= ntiles) break;
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (t + 2 < ntiles) issue_loads(t + 2, 1);
+            if ((t + 1) * BC < wave_kv_end) tile_math(TAIL, t + 1, smem, smem + 2 * TILE);
+        }
+    };
+    if (ntiles > 0) {
+        run_pass(std::true_type());
+        if (__syncthreads_or(big)) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+            m_run = -INFINITY;
+            l_run = 0.f;
+            run_pass(std::false_type());
+        }
     }
 
     // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l)
