@@ -35,6 +35,9 @@ struct KParams {
     const int32_t* __restrict__ key_lens;
     int H, Lq, Lk;
     int num_qb;        // query blocks per (b, h)
+    int num_items;     // work items = (b, h, query block) triples
+    int upi;           // work items per scheduling unit (1, or 2: a long/short pair)
+    int num_units;     // ceil(num_items / upi)
     float scale_log2;  // log2(e) / sqrt(d)
 };
 
@@ -110,6 +113,39 @@ __device__ __forceinline__ void map_workgroup(int num_qb, int* bh, int* qb) {
     *bh = lin / num_qb;
     int q = lin - *bh * num_qb;
     *qb = CAUSAL ? num_qb - 1 - q : q;
+}
+
+// Units of work for this workgroup: first, first + step, ... below last.
+// The grid is sized to the workgroups the GPU holds at once, and every
+// workgroup stays resident until all its units are done.  Workgroup ids are
+// dealt to the 8 XCDs in turn; each XCD gets a contiguous share of the units
+// (proportional to its workgroups) and its workgroups take those units
+// round-robin, so the workgroups running side by side on one XCD work on
+// neighbouring units -- the query blocks of a few heads, whose K and V then
+// stay in that XCD's L2.
+__device__ __forceinline__ void workgroup_units(int num_units, int* first, int* step, int* last) {
+    const int nwg = gridDim.x;
+    const int g = blockIdx.x;
+    const int xcd = g & 7, j = g >> 3;
+    const int per = nwg >> 3, rem = nwg & 7;
+    const int sx = per + (xcd < rem ? 1 : 0);
+    const int wlo = xcd * per + (xcd < rem ? xcd : rem);
+    const int ulo = (int)((long long)num_units * wlo / nwg);
+    const int uhi = (int)((long long)num_units * (wlo + sx) / nwg);
+    *first = ulo + j;
+    *step = sx;
+    *last = uhi;
+}
+
+// Work item -> (b*H + h, query block).  Causal query blocks of a head are
+// ordered longest, shortest, second longest, second shortest, ...: items
+// 2i and 2i + 1 of a head together take the same number of key tiles, so
+// scheduling units of such pairs are all equally long.
+template <bool CAUSAL>
+__device__ __forceinline__ void item_block(int item, int num_qb, int* bh, int* qb) {
+    *bh = item / num_qb;
+    const int q = item - *bh * num_qb;
+    *qb = !CAUSAL ? q : ((q & 1) ? (q >> 1) : num_qb - 1 - (q >> 1));
 }
 
 }  // namespace bf16k

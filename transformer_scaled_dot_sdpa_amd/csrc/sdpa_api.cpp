@@ -120,6 +120,7 @@ sdpa_status_t sdpa_forward(sdpa_handle_t h, const void* q, const void* k, const 
     sdpa::FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.key_lens = key_lens;
     a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk; a.d = d_k; a.causal = causal;
+    a.num_cus = h->num_cus;
 
     sdpa::Bf16Tile tile;
     if (h->dtype == SDPA_DTYPE_BF16) {

@@ -63,17 +63,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     static_assert((BC * CPR) % NT == 0, "tile must split evenly over threads");
     static_assert(BC % 32 == 0, "BC must be a multiple of 32");
 
-    // K[0], K[1], V[0], V[1]
-    extern __shared__ __align__(16) uint16_t smem[];
-
-    // ---- workgroup -> (b, h, query block).  Hardware hands consecutive
-    // workgroup ids to the 8 XCDs in turn; remap so that each XCD gets a
-    // contiguous range of work items (all query blocks of a head share that
-    // XCD's L2).  Causal: longest query blocks of a head first.
-    int bh, qb;
-    map_workgroup<CAUSAL>(p.num_qb, &bh, &qb);
-    const int b = bh / p.H;
-    const int q0 = qb * BR;
+    // K and V tiles, double buffered.  Four separate arrays rather than one:
+    // the compiler can then tell that the direct-to-LDS loads into one buffer
+    // never alias the reads of the other, and does not make those reads wait
+    // for the loads in flight (the tile barrier provides the real ordering).
+    __shared__ __align__(16) uint16_t k_lds0[TILE], k_lds1[TILE], v_lds0[TILE], v_lds1[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -81,6 +75,54 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31;   // query column inside the wave
     const int h = lane >> 5;   // which half of the 16-wide k slice
+
+    // ---- direct global -> LDS loads.  Load u of this thread fills LDS slot
+    // s = (wave*KCH + u)*64 + lane of the tile (16 bytes each).  The slot's
+    // (row, physical chunk) is fixed; the global source is chosen so that the
+    // swizzled / key-permuted layout comes out in LDS.  Buffer loads take the
+    // tile offset in a scalar register and the per-lane offset from a fixed
+    // register; the buffer ends at the valid key length, so rows past it
+    // arrive as zeros without being read.
+    uint32_t k_boff[KCH], v_boff[KCH];
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+        const int s = (wave * KCH + u) * 64 + lane;
+        const int row = s / CPR, pc = s % CPR;
+        k_boff[u] = (k_lds_row(row) * D + ((pc ^ k_swz<D>(row)) << 3)) * 2;
+        v_boff[u] = (row * D + ((pc ^ v_swz<D>(row)) << 3)) * 2;
+    }
+    // ---- per-lane LDS read offsets (elements) inside a tile
+    // K operand: row kt*32 + n, chunk (2ks + h) ^ swz  -> one base per ks,
+    // kt adds 32 rows.
+    int k_rd[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) k_rd[ks] = n * D + (((2 * ks + h) ^ k_swz<D>(n)) << 3);
+    // V operand (transposed read): rows kt*32 + 16ksl + 8h + 4r + li/4, column
+    // dt*32 + 16*((lane>>4)&1) + 4*(li&3).  The swizzle depends on row & 3,
+    // which the kt / ksl / r steps (multiples of 4) leave unchanged, so one
+    // base per dt suffices.
+    const int li = lane & 15;
+    int v_rd[NDT];
+    {
+        const int row = 8 * h + (li >> 2);
+        const int colg = 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int col = dt * 32 + colg;
+            v_rd[dt] = row * D + (((col >> 3) ^ v_swz<D>(row)) << 3) + (col & 7);
+        }
+    }
+
+    // ---- the workgroup's work items, one after the other (see
+    // workgroup_units and item_block for the schedule and the order)
+    int unit_first, unit_step, unit_last;
+    workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
+    for (int unit = unit_first; unit < unit_last; unit += unit_step)
+    for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
+    int bh, qb;
+    item_block<CAUSAL>(item, p.num_qb, &bh, &qb);
+    const int b = bh / p.H;
+    const int q0 = qb * BR;
 
     int kv_len = p.Lk;
     if (LENS) {
@@ -109,54 +151,28 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         for (int ks = 0; ks < NKS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
     }
 
-    // ---- direct global -> LDS loads.  Load u of this thread fills LDS slot
-    // s = (wave*KCH + u)*64 + lane of the tile (16 bytes each).  The slot's
-    // (row, physical chunk) is fixed; the global source is chosen so that the
-    // swizzled / key-permuted layout comes out in LDS.  Buffer loads take the
-    // tile offset in a scalar register and the per-lane offset from a fixed
-    // register; the buffer ends at the valid key length, so rows past it
-    // arrive as zeros without being read.
-    uint32_t k_boff[KCH], v_boff[KCH];
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-        const int s = (wave * KCH + u) * 64 + lane;
-        const int row = s / CPR, pc = s % CPR;
-        k_boff[u] = (k_lds_row(row) * D + ((pc ^ k_swz<D>(row)) << 3)) * 2;
-        v_boff[u] = (row * D + ((pc ^ v_swz<D>(row)) << 3)) * 2;
-    }
     const uint32_t kv_bytes = (uint32_t)kv_len * D * 2;
-    auto issue_loads = [&](int t, int buf) {
-        const uint32_t toff = (uint32_t)(t * BC) * D * 2;
-        lds_void* kd = (lds_void*)(smem + buf * TILE + wave * KCH * 64 * 8);
-        lds_void* vd = (lds_void*)(smem + (2 + buf) * TILE + wave * KCH * 64 * 8);
+    // Load u of K or V tile t into LDS buffer buf.  t < 0 asks for nothing:
+    // the buffer then has zero length and the load only writes zeros into a
+    // buffer no wavefront reads any more (so the instruction needs no branch
+    // around it and the surrounding MFMA code stays one block).
+    auto load_k = [&](int t, int buf, int u) __attribute__((always_inline)) {
+        const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * D * 2;
+        lds_void* kd = (lds_void*)((buf ? k_lds1 : k_lds0) + (wave * KCH + u) * 64 * 8);
+        buffer_load_lds16(kg, t < 0 ? 0u : kv_bytes, kd, k_boff[u], toff);
+    };
+    auto load_v = [&](int t, int buf, int u) __attribute__((always_inline)) {
+        const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * D * 2;
+        lds_void* vd = (lds_void*)((buf ? v_lds1 : v_lds0) + (wave * KCH + u) * 64 * 8);
+        buffer_load_lds16(vg, t < 0 ? 0u : kv_bytes, vd, v_boff[u], toff);
+    };
+    auto issue_loads = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < KCH; ++u) {
-            buffer_load_lds16(kg, kv_bytes, (lds_void*)((char*)kd + u * 1024), k_boff[u], toff);
-            buffer_load_lds16(vg, kv_bytes, (lds_void*)((char*)vd + u * 1024), v_boff[u], toff);
+            load_k(t, buf, u);
+            load_v(t, buf, u);
         }
     };
-
-    // ---- per-lane LDS read offsets (elements) inside a tile
-    // K operand: row kt*32 + n, chunk (2ks + h) ^ swz  -> one base per ks,
-    // kt adds 32 rows.
-    int k_rd[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) k_rd[ks] = n * D + (((2 * ks + h) ^ k_swz<D>(n)) << 3);
-    // V operand (transposed read): rows kt*32 + 16ksl + 8h + 4r + li/4, column
-    // dt*32 + 16*((lane>>4)&1) + 4*(li&3).  The swizzle depends on row & 3,
-    // which the kt / ksl / r steps (multiples of 4) leave unchanged, so one
-    // base per dt suffices.
-    const int li = lane & 15;
-    int v_rd[NDT];
-    {
-        const int row = 8 * h + (li >> 2);
-        const int colg = 16 * ((lane >> 4) & 1) + 4 * (li & 3);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const int col = dt * 32 + colg;
-            v_rd[dt] = row * D + (((col >> 3) ^ v_swz<D>(row)) << 3) + (col & 7);
-        }
-    }
 
     f32x16 o[NDT];
 #pragma unroll
@@ -172,8 +188,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     // against the fixed reference m_run and only records, per lane, whether
     // the tile's weights reached 2^64 (or were not finite); the exact path
     // (std::false_type) maintains the running maximum as usual.
-    auto tile_math = [&](auto FAST, int t, const uint16_t* Ks,
-                         const uint16_t* Vs) __attribute__((always_inline)) {
+    // The loads of the next tile (lt, into buffer lb; lt < 0: none) are
+    // spread over the tile's MFMAs -- K loads among the S products, V loads
+    // among the P.V products -- so that no wavefront stalls on a full
+    // memory-request queue, as it does when all of them issue at once.
+    auto tile_math = [&](auto FAST, int t, const uint16_t* Ks, const uint16_t* Vs, int lt,
+                         int lb) __attribute__((always_inline)) {
         const int ts = t * BC;
         // S^T = K Q^T, one 32-key sub-tile after the other so the softmax of
         // the first can start under the MFMAs of the second; operand reads
@@ -190,6 +210,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
                 if (ks + 1 < NKS)
                     ka[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[ks + 1]);
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1], qf[ks], s[kt], 0, 0, 0);
+                // K loads u in [i*KCH/NM, (i+1)*KCH/NM) after MFMA i of NM
+                constexpr int NM = NKT * NKS;
+                const int i = kt * NKS + ks;
+#pragma unroll
+                for (int u = i * KCH / NM; u < (i + 1) * KCH / NM; ++u) load_k(lt, lb, u);
             }
         }
 
@@ -206,6 +231,24 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
                     s[kt][r] = ok ? s[kt][r] : -INFINITY;
                 }
         }
+
+        // the transposed V reads of the first two key steps go out before
+        // the softmax, whose vector work covers their latency
+        constexpr int NSTEP = 2 * NKT;
+        i16x8 va[3][NDT];
+        auto read_v = [&](int step, i16x8* dst) __attribute__((always_inline)) {
+            const int roff = (step * 16) * D;   // step = 2*kt + ksl
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(Vs + roff + v_rd[dt]));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(Vs + roff + 4 * D + v_rd[dt]));
+                dst[dt] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        };
+        read_v(0, va[0]);
+        read_v(1, va[1]);
 
         bf16x8 pb[NKT][2];
         if constexpr (decltype(FAST)::value) {
@@ -254,34 +297,17 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         }
 
         // O^T += V^T P^T over 2*NKT key steps of 16; the NDT output chains
-        // interleave and the transposed V reads run one key step ahead.
-        constexpr int NSTEP = 2 * NKT;
-        i16x8 va[2][NDT];
-        auto read_v = [&](int step, i16x8* dst) {
-            const int roff = (step * 16) * D;   // step = 2*kt + ksl
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(Vs + roff + v_rd[dt]));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(Vs + roff + 4 * D + v_rd[dt]));
-                dst[dt] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-        };
-        read_v(0, va[0]);
+        // interleave, the transposed V reads run two key steps ahead and the
+        // V loads of the next tile are spread over the steps.
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
-            if (st + 1 < NSTEP) read_v(st + 1, va[(st + 1) & 1]);
+            if (st + 2 < NSTEP) read_v(st + 2, va[(st + 2) % 3]);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, va[st & 1][dt]), pb[st >> 1][st & 1], o[dt], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 1);
+                    __builtin_bit_cast(bf16x8, va[st % 3][dt]), pb[st >> 1][st & 1], o[dt], 0, 0, 0);
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) {
-            if (st + 1 < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, NDT, 1);
+            for (int u = st * KCH / NSTEP; u < (st + 1) * KCH / NSTEP; ++u) load_v(lt, lb, u);
         }
     };
 
@@ -296,19 +322,22 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         issue_loads(0, 0);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        if (1 < ntiles) issue_loads(1, 1);
-        tile_math(std::false_type(), 0, smem, smem + 2 * TILE);
+        tile_math(std::false_type(), 0, k_lds0, v_lds0, 1 < ntiles ? 1 : -1, 1);
         for (int t = 1; t < ntiles; t += 2) {
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
-            if (t + 1 < ntiles) issue_loads(t + 1, 0);
-            if (t * BC < wave_kv_end) tile_math(TAIL, t, smem + TILE, smem + 3 * TILE);
+            const int l0 = t + 1 < ntiles ? t + 1 : -1;
+            if (t * BC < wave_kv_end) tile_math(TAIL, t, k_lds1, v_lds1, l0, 0);
+            else if (l0 >= 0) issue_loads(l0, 0);
             if (t + 1 >= ntiles) break;
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
-            if (t + 2 < ntiles) issue_loads(t + 2, 1);
-            if ((t + 1) * BC < wave_kv_end) tile_math(TAIL, t + 1, smem, smem + 2 * TILE);
+            const int l1 = t + 2 < ntiles ? t + 2 : -1;
+            if ((t + 1) * BC < wave_kv_end) tile_math(TAIL, t + 1, k_lds0, v_lds0, l1, 1);
+            else if (l1 >= 0) issue_loads(l1, 1);
         }
+        // zero-length loads of the last tile may still be in flight
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     };
     if (ntiles > 0) {
         run_pass(std::true_type());
@@ -341,22 +370,16 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         if (p.lse != nullptr && h == 0)
             p.lse[(size_t)bh * p.Lq + qrow] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
     }
+    // every wavefront is done with both LDS buffers before the next item's
+    // first loads overwrite them
+    __syncthreads();
+    }
 }
 
 template <int D, int BC, int NW, bool CAUSAL, bool LENS>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     constexpr int BR = NW * 32;
-    const size_t lds = 4 * (size_t)BC * D * sizeof(uint16_t);
     auto kern = fwd_bf16_kernel<D, BC, NW, CAUSAL, LENS>;
-    if (lds > 65536) {
-        static bool attr_set = false;
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
-    }
     KParams p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -369,9 +392,16 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     p.Lk = a.Lk;
     p.num_qb = (a.Lq + BR - 1) / BR;
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const long long nwg = (long long)p.num_qb * a.B * a.H;
-    if (nwg <= 0 || nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), lds, stream, p);
+    const long long items = (long long)p.num_qb * a.B * a.H;
+    if (items <= 0 || items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    p.num_items = (int)items;
+    p.upi = CAUSAL ? 2 : 1;
+    p.num_units = (int)((items + p.upi - 1) / p.upi);
+    // one unit per workgroup: the hardware hands units to free slots as they
+    // come, which balances better than a fixed assignment; causal units are
+    // long/short pairs of equal length
+    const long long nwg = p.num_units;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 

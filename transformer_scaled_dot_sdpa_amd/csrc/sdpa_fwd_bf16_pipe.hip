@@ -1,29 +1,36 @@
-// Software-pipelined variant of the fused bf16 attention forward for gfx950.
+// Software-pipelined fused bf16 attention forward for gfx950.
 //
-// Same mathematics, layouts and masking as sdpa_fwd_bf16.hip (eq. (1) of
-// "Aufmerksamkeit ist alles, was Sie brauchen", section 3.2.1, with the
-// online softmax justified by the ratio identity of the formula page
-// "トランスフォーマーの注意機構", section 証明).  What differs is the order of
-// work inside a wavefront: keys are processed in 32-key sub-tiles j, and the
-// block of instructions for sub-tile j issues
-//     the MFMAs of S(j+1) = K_{j+1} Q^T        (matrix cores)
-//     the MFMAs of O += V_{j-1}^T P(j-1)^T     (matrix cores)
-//     the softmax of S(j): max, exp2, sum, bf16 pack   (vector ALU)
-// with no data dependence between the three, so the scheduler interleaves
-// vector work under the MFMAs of the same wavefront instead of relying on a
-// second wavefront being in the opposite phase.
+// Same mathematics, operand layouts, LDS layouts and masking rules as
+// sdpa_fwd_bf16.hip (eq. (1) of "Aufmerksamkeit ist alles, was Sie
+// brauchen", section 3.2.1, with the online softmax justified by the ratio
+// identity of the formula page "トランスフォーマーの注意機構", section 証明).
+// What differs is the order of work inside a wavefront.
 //
-// Rescaling.  softmax(j) may raise the reference maximum (lazily, when the
-// sub-tile maximum exceeds it by more than 2^8).  P(j-1), accumulated into O
-// in the same block, was formed with the old maximum, so the factor
-// alpha = 2^(m_old - m_new) is applied to O at the end of the block, after
-// that MFMA, and to the running sum before adding the new weights.
+// Keys are handled in 32-key sub-tiles j.  For each sub-tile there are
+// three steps: S(j) = K_j Q^T (NKS MFMAs), the softmax of S(j) into bf16
+// weights P(j) (vector ALU and exp), and O^T += V_j^T P(j)^T (2*NDT MFMAs).
+// Block b of the main loop issues
+//     S(b+2)   on the matrix cores,
+//     softmax of S(b+1) on the vector ALU,
+//     P(b).V   on the matrix cores,
+// which do not depend on each other, so every MFMA of the block has a few
+// vector instructions beside it: a wavefront keeps the matrix cores and the
+// vector ALU busy at the same time by itself, whatever the other wavefront
+// on its SIMD is doing.
 //
-// LDS.  K and V tiles of 64 keys, two buffers each (64 KiB per workgroup).
-// Block j reads K of sub-tile j+1 and V of sub-tile j-1; after every
-// even block both the K tile and the V tile that were just read for the
-// last time are free, so one barrier per tile lets the next K tile (two
-// tiles ahead) and the next V tile (one tile ahead) stream in.
+// Softmax: sub-tile 0 sets the reference maximum of each row exactly; later
+// sub-tiles take their exponentials against that fixed reference and only
+// record whether a sum of weights reached 2^64.  If one did anywhere in the
+// workgroup, the item is computed again with the exact online softmax, one
+// sub-tile after the other.
+//
+// LDS: K and V tiles of 64 keys (two sub-tiles), two buffers each, one
+// barrier per tile.  In the two blocks of tile T the reads are K(T+1) (for
+// S(2T+2), S(2T+3)) and V(T) (for P(2T).V, P(2T+1).V); at the barrier that
+// opens them, K(T+2) and V(T+1) start loading into the buffers that K(T)
+// and V(T-1) have just left.  Masks (causal diagonal, key length) can only
+// fall on a wavefront's last sub-tile, which is handled outside the
+// branch-free steady-state blocks.
 #include "sdpa_internal.h"
 #include "bf16_common.h"
 
@@ -39,7 +46,7 @@ template <int V>
 using IC = std::integral_constant<int, V>;
 
 template <int D, int NW, bool CAUSAL, bool LENS>
-__global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_pipe_kernel(KParams p) {
+__global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_pipe_kernel(KParams p) {
     constexpr int BC = 64;                     // keys per LDS tile
     constexpr int NT = NW * 64;
     constexpr int BR = NW * 32;
@@ -50,12 +57,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_pipe_kernel(KParams p) {
     constexpr int NKS = D / 16;                // k-steps of the Q.K^T product
     static_assert((BC * CPR) % NT == 0, "tile must split evenly over threads");
 
-    extern __shared__ __align__(16) uint16_t smem[];  // K[0], K[1], V[0], V[1]
-
-    int bh, qb;
-    map_workgroup<CAUSAL>(p.num_qb, &bh, &qb);
-    const int b = bh / p.H;
-    const int q0 = qb * BR;
+    __shared__ __align__(16) uint16_t k_lds0[TILE], k_lds1[TILE], v_lds0[TILE], v_lds1[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -63,34 +65,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_pipe_kernel(KParams p) {
     const int n = lane & 31;
     const int h = lane >> 5;
 
-    int kv_len = p.Lk;
-    if (LENS) {
-        int L = p.key_lens[b];
-        L = L < 0 ? 0 : L;
-        kv_len = L < kv_len ? L : kv_len;
-    }
-    const int kv_end = CAUSAL ? min(kv_len, q0 + BR) : kv_len;
-    const int ntiles = (kv_end + BC - 1) / BC;
-
-    const int q0w = q0 + wave * 32;
-    const int qrow = q0w + n;
-    const int wave_kv_end = CAUSAL ? min(kv_len, q0w + 32) : kv_len;
-    const int nsub = (wave_kv_end + 31) / 32;   // sub-tiles this wave computes
-
-    const size_t q_base = (size_t)bh * p.Lq * D;
-    const uint16_t* kg = p.k + (size_t)bh * p.Lk * D;
-    const uint16_t* vg = p.v + (size_t)bh * p.Lk * D;
-
-    // Q^T operand fragments (rows past Lq load the last valid row; never stored)
-    bf16x8 qf[NKS];
-    {
-        const int qr = qrow < p.Lq ? qrow : p.Lq - 1;
-        const i16x8* src = reinterpret_cast<const i16x8*>(p.q + q_base + (size_t)qr * D + 8 * h);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
-    }
-
-    // direct global -> LDS loads (see sdpa_fwd_bf16.hip for the layout)
+    // direct global -> LDS load slots (layout as in sdpa_fwd_bf16.hip)
     uint32_t k_boff[KCH], v_boff[KCH];
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
@@ -99,34 +74,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_pipe_kernel(KParams p) {
         k_boff[u] = (k_lds_row(row) * D + ((pc ^ k_swz<D>(row)) << 3)) * 2;
         v_boff[u] = (row * D + ((pc ^ v_swz<D>(row)) << 3)) * 2;
     }
-    auto issue = [&](const uint16_t* gbase, const uint32_t* boff, int t,
-                     uint16_t* lds_tile) __attribute__((always_inline)) {
-        if (t >= ntiles) return;
-        const int ts = t * BC;
-        const char* src = reinterpret_cast<const char*>(gbase + (size_t)ts * D);
-        lds_void* dst = (lds_void*)(lds_tile + wave * KCH * 64 * 8);
-        if (ts + BC <= kv_len) {
-#pragma unroll
-            for (int u = 0; u < KCH; ++u)
-                __builtin_amdgcn_global_load_lds((const void*)(src + boff[u]),
-                                                 (lds_void*)((char*)dst + u * 1024), 16, 0, 0);
-        } else {
-            const int last = kv_len - 1 - ts;
-#pragma unroll
-            for (int u = 0; u < KCH; ++u) {
-                const int r = (int)boff[u] / (2 * D), c = (int)boff[u] - r * 2 * D;
-                const uint32_t off = (uint32_t)((r < last ? r : last) * 2 * D + c);
-                __builtin_amdgcn_global_load_lds((const void*)(src + off),
-                                                 (lds_void*)((char*)dst + u * 1024), 16, 0, 0);
-            }
-        }
-    };
-    uint16_t* const Kbuf0 = smem;
-    uint16_t* const Kbuf1 = smem + TILE;
-    uint16_t* const Vbuf0 = smem + 2 * TILE;
-    uint16_t* const Vbuf1 = smem + 3 * TILE;
-
-    // per-lane LDS read offsets (elements); see sdpa_fwd_bf16.hip
+    // MFMA operand read offsets inside a tile (elements)
     int k_rd[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) k_rd[ks] = n * D + (((2 * ks + h) ^ k_swz<D>(n)) << 3);
@@ -141,146 +89,302 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_pipe_kernel(KParams p) {
             v_rd[dt] = row * D + (((col >> 3) ^ v_swz<D>(row)) << 3) + (col & 7);
         }
     }
+    const float sl = p.scale_log2;
+
+    int unit_first, unit_step, unit_last;
+    workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
+    for (int unit = unit_first; unit < unit_last; unit += unit_step)
+    for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
+    int bh, qb;
+    item_block<CAUSAL>(item, p.num_qb, &bh, &qb);
+    const int b = bh / p.H;
+    const int q0 = qb * BR;
+
+    int kv_len = p.Lk;
+    if (LENS) {
+        int L = p.key_lens[b];
+        L = L < 0 ? 0 : L;
+        kv_len = L < kv_len ? L : kv_len;
+    }
+    const int kv_end = CAUSAL ? min(kv_len, q0 + BR) : kv_len;
+    const int ntiles = (kv_end + BC - 1) / BC;
+    const int q0w = q0 + wave * 32;
+    const int qrow = q0w + n;
+    const int wave_kv_end = CAUSAL ? min(kv_len, q0w + 32) : kv_len;
+    const int nsub = wave_kv_end > 0 ? (wave_kv_end + 31) / 32 : 0;   // sub-tiles of this wave
+    // only the last sub-tile of a wavefront can cross the diagonal or the
+    // key length
+    const bool last_masked =
+        nsub > 0 && ((32 * nsub > kv_len) || (CAUSAL && 32 * nsub - 1 > q0w));
+
+    const size_t q_base = (size_t)bh * p.Lq * D;
+    const uint16_t* kg = p.k + (size_t)bh * p.Lk * D;
+    const uint16_t* vg = p.v + (size_t)bh * p.Lk * D;
+    const uint32_t kv_bytes = (uint32_t)kv_len * D * 2;
+
+    bf16x8 qf[NKS];
+    {
+        const int qr = qrow < p.Lq ? qrow : p.Lq - 1;
+        const i16x8* src = reinterpret_cast<const i16x8*>(p.q + q_base + (size_t)qr * D + 8 * h);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
+    }
+
+    auto load_k = [&](int t, uint16_t* buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < KCH; ++u)
+            buffer_load_lds16(kg, kv_bytes, (lds_void*)(buf + (wave * KCH + u) * 64 * 8), k_boff[u],
+                              (uint32_t)(t * BC) * D * 2);
+    };
+    auto load_v = [&](int t, uint16_t* buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < KCH; ++u)
+            buffer_load_lds16(vg, kv_bytes, (lds_void*)(buf + (wave * KCH + u) * 64 * 8), v_boff[u],
+                              (uint32_t)(t * BC) * D * 2);
+    };
+    // all loads issued so far have landed and every wavefront is past the
+    // reads of the previous tile
+    auto tile_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+    };
 
     f32x16 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    f32x16 sacc[2];
-    bf16x8 pb[2][2];
     float m_run = -INFINITY;   // reference maximum, exp2 units
     float l_run = 0.f;         // this lane's partial sum of weights
-    const float sl = p.scale_log2;
+    bool big = false;
 
-    // S^T of one 32-key sub-tile (position kt in the K tile at Ks)
-    auto s_product = [&](f32x16& acc, const uint16_t* Ks, int kt) __attribute__((always_inline)) {
-        bf16x8 ka[NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            ka[ks] = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[ks]);
+    // ---- sub-tile steps.  Accumulator r of lane (n, h) in S(j) holds key
+    // 32j + 16*(r/8) + 8h + r%8 of query row n (the K rows are permuted in
+    // LDS to make this so); P(j) keeps the same order as the B operand.
+    auto s_sub = [&](int j, const uint16_t* Kt) __attribute__((always_inline)) {
+        f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const uint16_t* base = Kt + (j & 1) * 32 * D;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *reinterpret_cast<const bf16x8*>(base + k_rd[ks]), qf[ks], acc, 0, 0, 0);
+        return acc;
     };
-
-    // One pipeline block for sub-tile j (see file header).  PAR = j & 1
-    // selects the register buffers; the K and V tiles are passed in.  Every
-    // block runs the same straight-line code: at the ends of the sequence
-    // the extra work is harmless (S of a sub-tile past the end is never
-    // used, a sub-tile past the wave's keys is fully masked, and P before
-    // the first sub-tile is zero against a zero-filled V buffer).
-    auto block = [&](auto PAR, const uint16_t* Ks, const uint16_t* Vs,
-                     int j) __attribute__((always_inline)) {
-        constexpr int par = decltype(PAR)::value;
-        constexpr int nxt = par ^ 1;
-        constexpr int kt = par ^ 1;   // position of sub-tiles j+1 and j-1 in their tiles
-        const int js = 32 * j;
-        if ((js + 32 > kv_len) || (CAUSAL && js + 31 > q0w)) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = js + 16 * (r >> 3) + 8 * h + (r & 7);
-                bool ok = key < kv_len;
-                if (CAUSAL) ok = ok && key <= qrow;
-                sacc[par][r] = ok ? sacc[par][r] : -INFINITY;
-            }
-        }
-        // softmax of S(j) (vector ALU)
-        float mx = sacc[par][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[par][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mt = mx * sl;
-        const bool raise = mt > m_run + kRescaleSlack;   // false when mt = -inf
-        const float mn = raise ? mt : m_run;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // 0 if m_run = -inf
-        const float mref = (mn == -INFINITY) ? 0.f : mn;
-        m_run = mn;
-        float lsum = 0.f;
+    auto mask_sub = [&](int j, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[par][r], sl, -mref));
-            lsum += pv;
-            pb[par][r >> 3][r & 7] = (__bf16)pv;
+            const int key = 32 * j + 16 * (r >> 3) + 8 * h + (r & 7);
+            bool ok = key < kv_len;
+            if (CAUSAL) ok = ok && key <= qrow;
+            s[r] = ok ? s[r] : -INFINITY;
         }
-        l_run = __builtin_fmaf(l_run, alpha, lsum);
-        // matrix cores: S(j+1) and O += V(j-1)^T P(j-1)^T, interleaved; each
-        // operand is read from LDS next to its MFMA (the scheduler hoists the
-        // reads as far as registers allow)
+    };
+    // fixed-reference weights
+    auto sm_fast = [&](const f32x16& s, bf16x8* pb) __attribute__((always_inline)) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[nxt][r] = 0.f;
-#pragma unroll
-        for (int i = 0; i < NKS; ++i) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[i]);
-            sacc[nxt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], sacc[nxt], 0, 0, 0);
-            if (i < 2 * NDT) {
-                const int ksl = i / NDT, dt = i % NDT;
-                const int roff = (kt * 32 + 16 * ksl) * D;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(Vs + roff + v_rd[dt]));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(Vs + roff + 4 * D + v_rd[dt]));
-                const i16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, va), pb[nxt][ksl], o[dt], 0, 0, 0);
-            }
+        for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl, -m_run));
+            part[r & 3] += pv;
+            pb[r >> 3][r & 7] = (__bf16)pv;
         }
-        // rescale O (rare) once P(j-1) has been accumulated; the empty asm
-        // keeps the compiler from executing the multiplies unconditionally
-        if (__ballot(alpha != 1.f) != 0ull) {
-            asm volatile("" ::: "memory");
+        const float lsum = (part[0] + part[1]) + (part[2] + part[3]);
+        l_run += lsum;
+        big |= !(lsum < 0x1p64f);
+    };
+    // exact online softmax step (rescales O when the maximum rises)
+    auto sm_exact = [&](const f32x16& s, bf16x8* pb) __attribute__((always_inline)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = max_across_halves(mx);
+        const float mt = mx * sl;
+        if (__ballot(mt > m_run + kRescaleSlack) != 0ull) {
+            const float mn = fmaxf(m_run, mt);
+            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+            l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            m_run = mn;
         }
+        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl, -mref));
+            l_run += pv;
+            pb[r >> 3][r & 7] = (__bf16)pv;
+        }
+    };
+    auto read_v = [&](const uint16_t* Vt, int j, int ksl, int dt) __attribute__((always_inline)) {
+        const uint16_t* a = Vt + ((j & 1) * 32 + 16 * ksl) * D + v_rd[dt];
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + 4 * D));
+        return __builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+    auto pv_sub = [&](int j, const uint16_t* Vt, const bf16x8* pb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ksl = 0; ksl < 2; ++ksl)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(Vt, j, ksl, dt), pb[ksl], o[dt],
+                                                                0, 0, 0);
+    };
+
+    // pipeline registers: block b reads (s_in = S(b+1), p_in = P(b)) and
+    // writes (S(b+2), P(b+1)); even blocks take set A as input, odd blocks B
+    f32x16 sA, sB;
+    bf16x8 pA[2], pB[2];
+
+    // steady-state block: S(b+2), softmax of S(b+1), P(b).V -- no branches.
+    // The block is cut into NKS steps, each holding one S MFMA, its share
+    // of the P.V MFMAs and of the softmax; operands are read a few steps
+    // before their MFMAs, and a scheduling fence between steps keeps the
+    // compiler from gathering the MFMAs in one place and the vector work in
+    // another.
+    auto block_full = [&](auto PAR, int bb, const uint16_t* Kt,
+                          const uint16_t* Vt) __attribute__((always_inline)) {
+        f32x16& s_in = PAR.value ? sB : sA;
+        f32x16& s_out = PAR.value ? sA : sB;
+        bf16x8* p_in = PAR.value ? pB : pA;
+        bf16x8* p_out = PAR.value ? pA : pB;
+        const uint16_t* kbase = Kt + ((bb + 2) & 1) * 32 * D;
+        constexpr int PER = 16 / NKS;        // softmax values per step
+        constexpr int PVM = 2 * NDT / NKS;   // P.V MFMAs per step
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        float part[2] = {0.f, 0.f};
+        constexpr int AHEAD = 2;             // steps the operand reads run ahead
+        bf16x8 kop[AHEAD + 1], vop[AHEAD + 1][PVM];
+        auto read_ops = [&](int i, int slot) __attribute__((always_inline)) {
+            kop[slot] = *reinterpret_cast<const bf16x8*>(kbase + k_rd[i]);
+#pragma unroll
+            for (int c = 0; c < PVM; ++c) {
+                const int q = i * PVM + c;
+                vop[slot][c] = read_v(Vt, bb, q / NDT, q % NDT);
+            }
+        };
+        auto softmax_part = [&](int r0, int r1) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = r0; r < r1; ++r) {
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_in[r], sl, -m_run));
+                part[r & 1] += pv;
+                p_out[r >> 3][r & 7] = (__bf16)pv;
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD && i < NKS; ++i) read_ops(i, i);
+#pragma unroll
+        for (int i = 0; i < NKS; ++i) {
+            if (i + AHEAD < NKS) read_ops(i + AHEAD, (i + AHEAD) % (AHEAD + 1));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % (AHEAD + 1)], qf[i], acc, 0, 0, 0);
+            softmax_part(i * PER, i * PER + PER / 2);
+#pragma unroll
+            for (int c = 0; c < PVM; ++c) {
+                const int q = i * PVM + c;
+                o[q % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i % (AHEAD + 1)][c], p_in[q / NDT],
+                                                                     o[q % NDT], 0, 0, 0);
+            }
+            softmax_part(i * PER + PER / 2, (i + 1) * PER);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const float lsum = part[0] + part[1];
+        l_run += lsum;
+        big |= !(lsum < 0x1p64f);
+        s_out = acc;
+    };
+    // the same block near the end of the wavefront's keys.  It runs whole:
+    // S(b+2) of a sub-tile past the wavefront's keys reads LDS contents that
+    // are never used, and the softmax of the last sub-tile, or of one past
+    // it, first masks the keys the row may not see (all of them, past the
+    // last sub-tile), so its weights are zero.  No register is updated
+    // conditionally, which keeps the pipeline registers from being doubled.
+    auto block_tail = [&](auto PAR, int bb, const uint16_t* Kt,
+                          const uint16_t* Vt) __attribute__((always_inline)) {
+        f32x16& s_in = PAR.value ? sB : sA;
+        if (bb + 1 > nsub - 1 || (bb + 1 == nsub - 1 && last_masked)) mask_sub(bb + 1, s_in);
+        block_full(PAR, bb, Kt, Vt);
+    };
+    auto pair = [&](int T, const uint16_t* Kt, const uint16_t* Vt) __attribute__((always_inline)) {
+        const int b0 = 2 * T;
+        if (b0 < nsub) block_tail(IC<0>(), b0, Kt, Vt);
+        if (b0 + 1 < nsub) block_tail(IC<1>(), b0 + 1, Kt, Vt);
     };
 
     if (ntiles > 0) {
-        // ---- prologue: K(0), V(0), K(1) in flight; zero V buffer 1 (read by
-        // the empty P.V of block 0); P starts at zero; then S(0)
-        issue(kg, k_boff, 0, Kbuf0);
-        issue(vg, v_boff, 0, Vbuf0);
-        issue(kg, k_boff, 1, Kbuf1);
-#pragma unroll
-        for (int i = tid; i < TILE / 8; i += NT)
-            reinterpret_cast<i16x8*>(Vbuf1)[i] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int y = 0; y < 2; ++y)
-                pb[x][y] = __builtin_bit_cast(bf16x8, i16x8{0, 0, 0, 0, 0, 0, 0, 0});
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-        s_product(sacc[0], Kbuf0, 0);
+        // prologue: K(0), V(0), K(1); S(0), S(1) and the exact softmax of
+        // sub-tile 0, which fixes the reference maximum
+        load_k(0, k_lds0);
+        load_v(0, v_lds0);
+        if (1 < ntiles) load_k(1, k_lds1);
+        tile_barrier();
+        if (nsub > 0) {
+            f32x16 s0 = s_sub(0, k_lds0);
+            if (nsub == 1 && last_masked) mask_sub(0, s0);
+            sA = s_sub(1, k_lds0);   // unused (masked) when nsub == 1
+            sm_exact(s0, pA);
+        }
+        for (int T = 0; T < ntiles; T += 2) {
+            tile_barrier();
+            if (T + 2 < ntiles) load_k(T + 2, k_lds0);
+            if (T + 1 < ntiles) load_v(T + 1, v_lds1);
+            pair(T, k_lds1, v_lds0);
+            if (T + 1 >= ntiles) break;
+            tile_barrier();
+            if (T + 3 < ntiles) load_k(T + 3, k_lds1);
+            if (T + 2 < ntiles) load_v(T + 2, v_lds0);
+            pair(T + 1, k_lds0, v_lds1);
+        }
 
-        // ---- blocks j = 0 .. nblocks (the last one drains P.V of the final
-        // sub-tile); four per trip so every buffer index is a constant.
-        // A wave skips the blocks past j = nsub (nothing left for it).
-        const int nblocks = 2 * ntiles;
-        for (int J = 0;; J += 4) {
-            const int T = J / 2;
-            if (J <= nsub) block(IC<0>(), Kbuf0, Vbuf1, J);   // S: tile T kt1; PV: tile T-1 kt1
-            if (J == nblocks) break;
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            __syncthreads();
-            issue(kg, k_boff, T + 2, Kbuf0);
-            issue(vg, v_boff, T + 1, Vbuf1);
-            if (J + 1 <= nsub) block(IC<1>(), Kbuf1, Vbuf0, J + 1);   // S: tile T+1 kt0; PV: tile T kt0
-            if (J + 2 <= nsub) block(IC<0>(), Kbuf1, Vbuf0, J + 2);   // S: tile T+1 kt1; PV: tile T kt1
-            if (J + 2 == nblocks) break;
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            __syncthreads();
-            issue(kg, k_boff, T + 3, Kbuf1);
-            issue(vg, v_boff, T + 2, Vbuf0);
-            if (J + 3 <= nsub) block(IC<1>(), Kbuf0, Vbuf1, J + 3);   // S: tile T+2 kt0; PV: tile T+1 kt0
+        // a fixed-reference sum reached 2^64 somewhere: exact pass, one
+        // sub-tile after the other, K(T) and V(T) both in buffer T & 1
+        if (__syncthreads_or(big)) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+            m_run = -INFINITY;
+            l_run = 0.f;
+            auto exact_tile = [&](int T, const uint16_t* Kt,
+                                  const uint16_t* Vt) __attribute__((always_inline)) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j = 2 * T + jj;
+                    if (j < nsub) {
+                        f32x16 s = s_sub(j, Kt);
+                        if (j == nsub - 1 && last_masked) mask_sub(j, s);
+                        bf16x8 pb[2];
+                        sm_exact(s, pb);
+                        pv_sub(j, Vt, pb);
+                    }
+                }
+            };
+            load_k(0, k_lds0);
+            load_v(0, v_lds0);
+            for (int T = 0; T < ntiles; T += 2) {
+                tile_barrier();
+                if (T + 1 < ntiles) {
+                    load_k(T + 1, k_lds1);
+                    load_v(T + 1, v_lds1);
+                }
+                exact_tile(T, k_lds0, v_lds0);
+                if (T + 1 >= ntiles) break;
+                tile_barrier();
+                if (T + 2 < ntiles) {
+                    load_k(T + 2, k_lds0);
+                    load_v(T + 2, v_lds0);
+                }
+                exact_tile(T + 1, k_lds1, v_lds1);
+            }
         }
     }
 
     // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l)
-    const float l = l_run + __shfl_xor(l_run, 32);
+    const float l = sum_across_halves(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (qrow < p.Lq) {
         uint16_t* dst = p.out + q_base + (size_t)qrow * D;
@@ -297,12 +401,15 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_pipe_kernel(KParams p) {
         if (p.lse != nullptr && h == 0)
             p.lse[(size_t)bh * p.Lq + qrow] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
     }
+    // both LDS buffers are free before the next item's first loads
+    __syncthreads();
+    }
 }
 
 template <int D, int NW, bool CAUSAL, bool LENS>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     constexpr int BR = NW * 32;
-    const size_t lds = 4 * (size_t)64 * D * sizeof(uint16_t);
+    auto kern = fwd_bf16_pipe_kernel<D, NW, CAUSAL, LENS>;
     KParams p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -315,10 +422,12 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     p.Lk = a.Lk;
     p.num_qb = (a.Lq + BR - 1) / BR;
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const long long nwg = (long long)p.num_qb * a.B * a.H;
-    if (nwg <= 0 || nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, NW, CAUSAL, LENS>), dim3((unsigned)nwg),
-                       dim3(NW * 64), lds, stream, p);
+    const long long items = (long long)p.num_qb * a.B * a.H;
+    if (items <= 0 || items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    p.num_items = (int)items;
+    p.upi = CAUSAL ? 2 : 1;
+    p.num_units = (int)((items + p.upi - 1) / p.upi);
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.num_units), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ struct FwdArgs {
     const int32_t* key_lens;  // device int32[B], may be null
     int B, H, Lq, Lk, d;
     int causal;
+    int num_cus;              // compute units of the device (sizes persistent grids)
 };
 
 // One bf16 tile configuration.  br = rows of Q per workgroup
