@@ -19,7 +19,11 @@ in HBM.  W untimed steps, then K timed steps bracketed by
   source, else null;
 * ``cpu_baseline``: the fp64 CPU oracle timed on this host on a bounded
   sample of the same workload (whole (b, h) slices), TFLOP/s by the same
-  headline formula.
+  headline formula;
+* ``vendor_gemm``: context for the MFMA roofline -- the rate torch.matmul
+  (the vendor BLAS) reaches on a large square bf16 product on the same GPU in
+  the same run, i.e. what dense matrix cores deliver in practice at the clock
+  the chip holds under full MFMA load, and ``value`` as a fraction of it.
 
 Only one GPU is used; ``--gpus`` above 1 exits with a message.
 """
@@ -42,6 +46,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop / byte
 KERNEL_SOURCES = ["transformer_scaled_dot_sdpa_amd/csrc/sdpa_fwd_bf16.hip",
+                  "transformer_scaled_dot_sdpa_amd/csrc/bf16_common.h",
                   "transformer_scaled_dot_sdpa_amd/csrc/tile_select.cpp"]
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -143,6 +148,26 @@ def copy_calibration(mib: int):
     return {"copy_calibration_bytes": n, "copies": 3}
 
 
+def vendor_gemm(torch, m: int = 16384, n: int = 16384, k: int = 8192, iters: int = 10):
+    """TFLOP/s of torch.matmul on an (m x k) by (k x n) bf16 product (contiguous operands)."""
+    a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del a, b, c
+    return {"value": 2.0 * m * n * k / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "kind": f"torch.matmul bf16 ({m}x{k}) by ({k}x{n})", "ms": ms}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +177,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip the vendor GEMM context measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -263,6 +290,11 @@ def main():
                    "input_scale": w.scale, "seed": w.seed, "input_sets": nsets},
         "roofline": roof,
     }
+    if not args.no_vendor_gemm:
+        g = vendor_gemm(torch)
+        g["attention_value_over_gemm"] = value / g["value"]
+        result["vendor_gemm"] = g
+        print(f"[bench] vendor GEMM {g['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         a = sets[(args.steps - 1) % nsets]

@@ -418,6 +418,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s) {
     if (t.kind == 1) return launch_fwd_bf16_pipe(a, t, s);
     if (t.kind == 2) return launch_fwd_bf16_pp(a, t, s);
+    if (t.kind == 3) return launch_fwd_bf16_wide(a, t, s);
     if (t.d == 128 && t.bc == 64 && t.waves == 4) return launch_d<128, 64, 4>(a, s);
     if (t.d == 128 && t.bc == 64 && t.waves == 8) return launch_d<128, 64, 8>(a, s);
     if (t.d == 64 && t.bc == 64 && t.waves == 4) return launch_d<64, 64, 4>(a, s);

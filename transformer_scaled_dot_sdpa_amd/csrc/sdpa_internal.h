@@ -27,7 +27,8 @@ struct Bf16Tile {
     int d;
     int bc;
     int waves;
-    int kind;   // 0: sdpa_fwd_bf16.hip, 1: sdpa_fwd_bf16_pipe.hip, 2: sdpa_fwd_bf16_pp.hip
+    int kind;   // 0: sdpa_fwd_bf16.hip, 1: sdpa_fwd_bf16_pipe.hip, 2: sdpa_fwd_bf16_pp.hip,
+                // 3: sdpa_fwd_bf16_wide.hip
     const char* name;
 };
 
@@ -40,6 +41,7 @@ bool select_bf16_tile(int d, int causal, long long bh, int Lq, int Lk, int num_c
 hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_bf16_pipe(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_bf16_pp(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
+hipError_t launch_fwd_bf16_wide(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 
 }  // namespace sdpa
