@@ -103,6 +103,9 @@ class Oracle:
         lib.oracle_sdpa_rows.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64,
                                          i32, vp, dbl, vp, i64, vp, vp, i32]
         lib.oracle_sdpa_rows.restype = i32
+        lib.oracle_sdpa_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64,
+                                        i32, vp, dbl, vp, vp, vp, i32]
+        lib.oracle_sdpa_bwd.restype = i32
         self._lib = lib
         self.path = lib_path
 
@@ -158,6 +161,34 @@ class Oracle:
         return out, lse
 
 
+    def sdpa_bwd(self, q, k, v, dout, causal: bool = False, key_lens=None,
+                 tau: float | None = None, bf16: bool = False, nthreads: int = 0):
+        """Gradients of a loss L with dL/d(out) = ``dout`` ([B, H, Lq, d], same
+        dtype as q): returns ``(dq, dk, dv)`` in fp64, shaped like q, k, v."""
+        q, dt = _as_input(q, bf16)
+        k, dtk = _as_input(k, bf16)
+        v, dtv = _as_input(v, bf16)
+        dout, dto = _as_input(dout, bf16)
+        if not (dt == dtk == dtv == dto):
+            raise TypeError("q, k, v, dout must share one dtype")
+        B, H, Lq, Lk, d = _check_shapes(q, k, v)
+        if dout.shape != q.shape:
+            raise ValueError("dout must have the shape of q")
+        _kl, kl_ptr = _key_lens_arg(key_lens, B)
+        dq = np.empty((B, H, Lq, d), dtype=np.float64)
+        dk = np.empty((B, H, Lk, d), dtype=np.float64)
+        dv = np.empty((B, H, Lk, d), dtype=np.float64)
+        rc = self._lib.oracle_sdpa_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                       dout.ctypes.data, dt, B, H, Lq, Lk, d,
+                                       int(bool(causal)), kl_ptr,
+                                       float(tau) if tau is not None else 0.0,
+                                       dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                       int(nthreads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_sdpa_bwd failed with code {rc}")
+        return dq, dk, dv
+
+
 _lock = threading.Lock()
 _default: Oracle | None = None
 
@@ -179,3 +210,8 @@ def sdpa(q, k, v, **kw):
 def sdpa_rows(q, k, v, rows, **kw):
     """:meth:`Oracle.sdpa_rows` of the default oracle."""
     return default().sdpa_rows(q, k, v, rows, **kw)
+
+
+def sdpa_bwd(q, k, v, dout, **kw):
+    """:meth:`Oracle.sdpa_bwd` of the default oracle."""
+    return default().sdpa_bwd(q, k, v, dout, **kw)

@@ -68,3 +68,55 @@ def attention(q, k, v, causal=False, key_lens=None, tau=None):
         out.append(ob)
         lse.append(lb)
     return out, lse
+
+
+def attention_grad(q, k, v, dout, causal=False, key_lens=None, tau=None):
+    """Gradients (dq, dk, dv) of a loss L with dL/d(out) = ``dout``.
+
+    Written out with the full Jacobian matrix of the weights, as the proof
+    section (証明) of the formula page prints it: da_j/ds_l = a_j (delta_jl -
+    a_l).  For every query row: dL/da_j = dout . v_j (from o = sum_j a_j v_j),
+    dL/ds_l = sum_j dL/da_j * J[j][l], then dL/dq = sum_l dL/ds_l k_l / tau,
+    dL/dk_l += dL/ds_l q / tau and dL/dv_j += a_j dout.  Nested lists in and
+    out, shapes as in :func:`attention`.
+    """
+    B, H = len(q), len(q[0])
+    d = len(q[0][0][0])
+    if tau is None:
+        tau = math.sqrt(d)
+    dq = [[[[0.0] * d for _ in q[b][h]] for h in range(H)] for b in range(B)]
+    dk = [[[[0.0] * d for _ in k[b][h]] for h in range(H)] for b in range(B)]
+    dv = [[[[0.0] * d for _ in v[b][h]] for h in range(H)] for b in range(B)]
+    for b in range(B):
+        for h in range(H):
+            Lk = len(k[b][h])
+            # per key, the list of terms of dk and dv, summed at the end
+            tk = [[[] for _ in range(d)] for _ in range(Lk)]
+            tv = [[[] for _ in range(d)] for _ in range(Lk)]
+            for i in range(len(q[b][h])):
+                n = Lk
+                if key_lens is not None:
+                    n = min(n, max(0, int(key_lens[b])))
+                if causal:
+                    n = min(n, i + 1)
+                if n == 0:
+                    continue
+                qi = [float(x) for x in q[b][h][i]]
+                gi = [float(x) for x in dout[b][h][i]]
+                s = [math.fsum(qi[t] * float(k[b][h][j][t]) for t in range(d)) / tau for j in range(n)]
+                e = [math.exp(x) for x in s]
+                Z = math.fsum(e)
+                a = [x / Z for x in e]
+                da = [math.fsum(gi[t] * float(v[b][h][j][t]) for t in range(d)) for j in range(n)]
+                jac = [[a[j] * ((1.0 if j == l else 0.0) - a[l]) for l in range(n)] for j in range(n)]
+                ds = [math.fsum(da[j] * jac[j][l] for j in range(n)) for l in range(n)]
+                dq[b][h][i] = [math.fsum(ds[l] * float(k[b][h][l][t]) for l in range(n)) / tau
+                               for t in range(d)]
+                for l in range(n):
+                    for t in range(d):
+                        tk[l][t].append(ds[l] * qi[t] / tau)
+                        tv[l][t].append(a[l] * gi[t])
+            for j in range(Lk):
+                dk[b][h][j] = [math.fsum(tk[j][t]) for t in range(d)]
+                dv[b][h][j] = [math.fsum(tv[j][t]) for t in range(d)]
+    return dq, dk, dv

@@ -41,6 +41,17 @@
  *
  * Inputs may be fp64, fp32 or bf16 (raw 16-bit patterns); every element is
  * widened to fp64 exactly before any arithmetic.  Outputs are fp64.
+ *
+ * Backward (oracle_sdpa_bwd): the gradients of a scalar loss L with
+ * dL/dO = dout, following the same proof section:
+ *   dL/da_j = dout . v_j                    (from the output display)
+ *   dL/ds_l = sum_j dL/da_j * da_j/ds_l,  with the page's Jacobian display
+ *             da_j/ds_l = a_j (delta_jl - a_l),
+ *           = a_l (dL/da_l - sum_j a_j dL/da_j)
+ *   dL/dq   = sum_l dL/ds_l k_l / tau,  dL/dk_l += dL/ds_l q / tau  (score)
+ *   dL/dv_j += a_j dout                     (output display)
+ * summed over the query rows of each (b, h) slice.  Masked keys have a_j = 0
+ * and receive nothing; a row with no valid key contributes nothing.
  */
 #include <math.h>
 #include <stdint.h>
@@ -67,16 +78,14 @@ static double load_elem(const void* base, int dtype, int64_t idx)
  * q_off, kv_off: element offsets of the row of Q and of the (b, h) slice of
  * K and V.
  */
-static void attention_row(const void* q, const void* k, const void* v,
-                          int dtype, int64_t q_off, int64_t kv_off,
-                          int64_t d, int64_t n_valid, double tau,
-                          double* o, double* lse, double* work)
+/*
+ * Steps 1 and 2 for one query row with n_valid >= 1 keys: work[j] = a_j.
+ * Returns m + ln Z (step 4).
+ */
+static double row_weights(const void* q, const void* k, int dtype, int64_t q_off,
+                          int64_t kv_off, int64_t d, int64_t n_valid, double tau,
+                          double* work)
 {
-    if (n_valid <= 0) {
-        for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
-        *lse = -INFINITY;
-        return;
-    }
     /* 1. scores */
     for (int64_t j = 0; j < n_valid; ++j) {
         double z = 0.0;
@@ -94,6 +103,21 @@ static void attention_row(const void* q, const void* k, const void* v,
         Z += work[j];
     }
     for (int64_t j = 0; j < n_valid; ++j) work[j] /= Z;
+    /* 4. log-sum-exp of the valid scores */
+    return m + log(Z);
+}
+
+static void attention_row(const void* q, const void* k, const void* v,
+                          int dtype, int64_t q_off, int64_t kv_off,
+                          int64_t d, int64_t n_valid, double tau,
+                          double* o, double* lse, double* work)
+{
+    if (n_valid <= 0) {
+        for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    *lse = row_weights(q, k, dtype, q_off, kv_off, d, n_valid, tau, work);
     /* 3. output: weighted sum of the value rows */
     for (int64_t t = 0; t < d; ++t) {
         double acc = 0.0;
@@ -101,8 +125,6 @@ static void attention_row(const void* q, const void* k, const void* v,
             acc += work[j] * load_elem(v, dtype, kv_off + j * d + t);
         o[t] = acc;
     }
-    /* 4. log-sum-exp of the valid scores */
-    *lse = m + log(Z);
 }
 
 /* Number of valid keys for query row i of batch b. */
@@ -203,6 +225,67 @@ int oracle_sdpa(const void* q, const void* k, const void* v, int dtype,
                           out + row * d, lse + row, work);
         }
         free(work);
+    }
+    return bad ? 2 : 0;
+}
+
+/*
+ * Gradients.  q, dout, dq are [B, H, Lq, d]; k, v, dk, dv are [B, H, Lk, d];
+ * all contiguous row-major; dout has the inputs' dtype, dq/dk/dv are fp64.
+ * Slices are independent and run in parallel; inside a slice the query rows
+ * are taken in order, so dk and dv are summed in a fixed order.
+ */
+int oracle_sdpa_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                    int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                    int causal, const int32_t* key_lens, double tau,
+                    double* dq, double* dk, double* dv, int nthreads)
+{
+    if (!dout || !dq || !dk || !dv) return 1;
+    if (check_args(q, k, v, dtype, B, H, Lq, Lk, d, causal, dq, dk)) return 1;
+    if (!(tau > 0.0)) tau = sqrt((double)d);
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    int bad = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* a = (double*)malloc(sizeof(double) * (size_t)Lk);
+        double* da = (double*)malloc(sizeof(double) * (size_t)Lk);
+        if (!a || !da) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * H; ++bh) {
+            if (!a || !da) continue;
+            const int64_t b = bh / H;
+            const int64_t kv_off = bh * Lk * d;
+            for (int64_t x = 0; x < Lk * d; ++x) dk[kv_off + x] = dv[kv_off + x] = 0.0;
+            for (int64_t i = 0; i < Lq; ++i) {
+                const int64_t q_off = (bh * Lq + i) * d;
+                for (int64_t t = 0; t < d; ++t) dq[q_off + t] = 0.0;
+                const int64_t n_valid = valid_keys(i, b, Lk, causal, key_lens);
+                if (n_valid <= 0) continue;
+                row_weights(q, k, dtype, q_off, kv_off, d, n_valid, tau, a);
+                /* dL/da_j = dout . v_j and c = sum_j a_j dL/da_j */
+                double c = 0.0;
+                for (int64_t j = 0; j < n_valid; ++j) {
+                    double z = 0.0;
+                    for (int64_t t = 0; t < d; ++t)
+                        z += load_elem(dout, dtype, q_off + t) * load_elem(v, dtype, kv_off + j * d + t);
+                    da[j] = z;
+                    c += a[j] * z;
+                }
+                for (int64_t j = 0; j < n_valid; ++j) {
+                    const double ds = a[j] * (da[j] - c);   /* dL/ds_j */
+                    for (int64_t t = 0; t < d; ++t) {
+                        dq[q_off + t] += ds * load_elem(k, dtype, kv_off + j * d + t) / tau;
+                        dk[kv_off + j * d + t] += ds * load_elem(q, dtype, q_off + t) / tau;
+                        dv[kv_off + j * d + t] += a[j] * load_elem(dout, dtype, q_off + t);
+                    }
+                }
+            }
+        }
+        free(a);
+        free(da);
     }
     return bad ? 2 : 0;
 }

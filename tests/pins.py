@@ -364,10 +364,115 @@ def pin_input_widening(orc):
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+# --------------------------------------------------------------------------
+# Backward: gradients of a loss L given dL/d(out)
+# --------------------------------------------------------------------------
+
+def pin_bwd_two_keys_gradient(orc):
+    """The two-key example of section 応用 seen through the gradient.  With
+    v_1 = e_0, v_2 = 0 and dL/d(out) = e_0 the loss is a_1, so the Jacobian
+    display gives dL/ds_1 = a_1 (1 - a_1) and dL/ds_2 = -a_1 a_2: the page's
+    gradient factor, 0.197 scaled and 0.0003 unscaled.  It is read off dq
+    (= sum_l dL/ds_l k_l / tau with k_1 = e_0, k_2 = 0); dk_1, dk_2 and dv_1
+    follow from the same numbers."""
+    g = _golden("two_keys_d64.json")
+    d, gap = g["d_k"], g["dot_product_gap"]
+    pr = g["printed"]
+    q = np.zeros((1, 1, 1, d)); q[..., 0] = gap
+    k = np.zeros((1, 1, 2, d)); k[0, 0, 0, 0] = 1.0
+    v = np.zeros((1, 1, 2, d)); v[0, 0, 0, 0] = 1.0
+    gout = np.zeros((1, 1, 1, d)); gout[..., 0] = 1.0
+    for tau, key, dec in ((math.sqrt(d), "scaled_a_one_minus_a", 3),
+                          (1.0, "unscaled_a_one_minus_a", 4)):
+        dq, dk, dv = orc.sdpa_bwd(q, k, v, gout, tau=tau)
+        ds1 = dq[0, 0, 0, 0] * tau
+        assert _printed_close(ds1, pr[key]["value"], dec), (tau, ds1)
+        assert np.allclose(dq[0, 0, 0, 1:], 0.0)
+        assert abs(dk[0, 0, 0, 0] - ds1 * gap / tau) < 1e-12
+        assert abs(dk[0, 0, 1, 0] + ds1 * gap / tau) < 1e-12
+        a1 = 0.5 + math.sqrt(0.25 - ds1)          # root of a(1-a) = ds1 above 1/2
+        assert abs(dv[0, 0, 0, 0] - a1) < 1e-9 and abs(dv[0, 0, 1, 0] - (1 - a1)) < 1e-9
+
+
+def pin_bwd_finite_differences(orc, seed=21):
+    """Central differences of the (pinned) forward: each gradient entry equals
+    (L(x + h) - L(x - h)) / 2h with L = sum(dout * out), on tiny fp64 problems
+    with and without masks."""
+    rng = np.random.default_rng(seed)
+    h = 1e-6
+    for causal, kl in ((False, None), (True, None), (False, [3, 0]), (True, [5, 2])):
+        B, H, Lq, Lk, d = 2, 1, 4, 5, 3
+        q = rng.standard_normal((B, H, Lq, d))
+        k = rng.standard_normal((B, H, Lk, d))
+        v = rng.standard_normal((B, H, Lk, d))
+        gout = rng.standard_normal((B, H, Lq, d))
+        grads = orc.sdpa_bwd(q, k, v, gout, causal=causal, key_lens=kl)
+
+        def loss():
+            out, _ = orc.sdpa(q, k, v, causal=causal, key_lens=kl)
+            return float(np.sum(out * gout))
+        for arr, grad in zip((q, k, v), grads):
+            for idx in np.ndindex(arr.shape):
+                x0 = arr[idx]
+                arr[idx] = x0 + h
+                lp = loss()
+                arr[idx] = x0 - h
+                lm = loss()
+                arr[idx] = x0
+                assert abs((lp - lm) / (2 * h) - grad[idx]) < 1e-6, (causal, kl, idx)
+
+
+def pin_bwd_brute_force(orc, seed=22):
+    """The C gradients equal the full-Jacobian pure-Python route
+    (oracle/brute.py) to 1e-12 on the toy shapes."""
+    from oracle import brute
+    rng = np.random.default_rng(seed)
+    for (B, H, Lq, Lk, d, causal, kl) in ((1, 2, 8, 8, 3, False, None),    # toy encoder
+                                          (1, 2, 4, 4, 3, True, None),     # toy decoder
+                                          (1, 2, 4, 8, 3, False, None),    # toy cross
+                                          (2, 1, 5, 6, 4, True, [4, 0])):
+        q = rng.standard_normal((B, H, Lq, d))
+        k = rng.standard_normal((B, H, Lk, d))
+        v = rng.standard_normal((B, H, Lk, d))
+        gout = rng.standard_normal((B, H, Lq, d))
+        got = orc.sdpa_bwd(q, k, v, gout, causal=causal, key_lens=kl)
+        ref = brute.attention_grad(q.tolist(), k.tolist(), v.tolist(), gout.tolist(), causal, kl)
+        for a, b in zip(got, ref):
+            assert np.max(np.abs(a - np.array(b))) < 1e-12
+
+
+def pin_bwd_invariants(orc, seed=23):
+    """Weights sum to 1 and depend only on score differences, so per row the
+    score gradients sum to 0: the key gradients of a slice sum to 0, and the
+    value gradients sum to the dL/d(out) rows that see any key.  Keys nobody
+    sees and rows that see no key get exactly zero."""
+    rng = np.random.default_rng(seed)
+    B, H, Lq, Lk, d = 2, 2, 6, 7, 4
+    kl = [5, 0]
+    for causal in (False, True):
+        q = rng.standard_normal((B, H, Lq, d))
+        k = rng.standard_normal((B, H, Lk, d))
+        v = rng.standard_normal((B, H, Lk, d))
+        gout = rng.standard_normal((B, H, Lq, d))
+        dq, dk, dv = orc.sdpa_bwd(q, k, v, gout, causal=causal, key_lens=kl)
+        for b in range(B):
+            n = min(Lk, kl[b])
+            seen = [i for i in range(Lq) if (min(n, i + 1) if causal else n) > 0]
+            for hh in range(H):
+                assert np.max(np.abs(dk[b, hh].sum(axis=0))) < 1e-12
+                want = gout[b, hh, seen].sum(axis=0) if seen else np.zeros(d)
+                assert np.max(np.abs(dv[b, hh].sum(axis=0) - want)) < 1e-12
+                assert np.all(dk[b, hh, n:] == 0) and np.all(dv[b, hh, n:] == 0)
+                unseen = [i for i in range(Lq) if i not in seen]
+                assert np.all(dq[b, hh, unseen] == 0)
+
+
 ALL_PINS = [
     pin_worked_example_output, pin_worked_example_weights, pin_worked_example_scores,
     pin_temperature, pin_two_keys_d64, pin_softmax_row_properties,
     pin_temperature_limits, pin_causal, pin_padding, pin_lse_bounds,
     pin_shift_invariance, pin_score_variance, pin_head_batch_permutation,
     pin_brute_force, pin_rows_match_full, pin_input_widening,
+    pin_bwd_two_keys_gradient, pin_bwd_finite_differences, pin_bwd_brute_force,
+    pin_bwd_invariants,
 ]

@@ -15,8 +15,8 @@ MUTANTS = [
     ("no_scale", "work[j] = z / tau;", "work[j] = z;"),
     ("multiply_by_tau", "work[j] = z / tau;", "work[j] = z * tau;"),
     ("no_normalisation", "for (int64_t j = 0; j < n_valid; ++j) work[j] /= Z;", ""),
-    ("lse_drops_max", "*lse = m + log(Z);", "*lse = log(Z);"),
-    ("lse_log2", "*lse = m + log(Z);", "*lse = m + log2(Z);"),
+    ("lse_drops_max", "return m + log(Z);", "return log(Z);"),
+    ("lse_log2", "return m + log(Z);", "return m + log2(Z);"),
     ("max_shift_sign", "work[j] = exp(work[j] - m);", "work[j] = exp(work[j] + m);"),
     ("causal_masks_diagonal", "if (causal && i + 1 < hi) hi = i + 1;", "if (causal && i < hi) hi = i;"),
     ("causal_ignored", "if (causal && i + 1 < hi) hi = i + 1;", ""),
@@ -34,6 +34,17 @@ MUTANTS = [
      "uint32_t bits = (uint32_t)((const uint16_t*)base)[idx];"),
     ("wrong_head_offset", "bh * Lk * d, d, n_valid, tau,\n                          out + row * d",
      "b * Lk * d, d, n_valid, tau,\n                          out + row * d"),
+    # backward
+    ("bwd_no_centering", "const double ds = a[j] * (da[j] - c);", "const double ds = a[j] * da[j];"),
+    ("bwd_centering_unweighted", "c += a[j] * z;", "c += z;"),
+    ("bwd_dq_no_scale", "dq[q_off + t] += ds * load_elem(k, dtype, kv_off + j * d + t) / tau;",
+     "dq[q_off + t] += ds * load_elem(k, dtype, kv_off + j * d + t);"),
+    ("bwd_dk_from_k", "dk[kv_off + j * d + t] += ds * load_elem(q, dtype, q_off + t) / tau;",
+     "dk[kv_off + j * d + t] += ds * load_elem(k, dtype, kv_off + j * d + t) / tau;"),
+    ("bwd_dv_from_da", "dv[kv_off + j * d + t] += a[j] * load_elem(dout, dtype, q_off + t);",
+     "dv[kv_off + j * d + t] += da[j] * load_elem(dout, dtype, q_off + t);"),
+    ("bwd_da_from_k", "z += load_elem(dout, dtype, q_off + t) * load_elem(v, dtype, kv_off + j * d + t);",
+     "z += load_elem(dout, dtype, q_off + t) * load_elem(k, dtype, kv_off + j * d + t);"),
 ]
 
 
