@@ -1,5 +1,6 @@
 /*
- * sdpa.h -- C ABI of the MI355X (gfx950) scaled dot-product attention forward.
+ * sdpa.h -- C ABI of the MI355X (gfx950) scaled dot-product attention forward
+ * and its gradients.
  *
  * The operation is eq. (1) of "Aufmerksamkeit ist alles, was Sie brauchen"
  * (German translation of "Attention Is All You Need"), section 3.2.1:
@@ -98,6 +99,55 @@ sdpa_status_t sdpa_forward(sdpa_handle_t h,
                            void* out, float* lse,
                            int B, int H, int Lq, int Lk, int d_k,
                            int causal, const int32_t* key_lens, void* stream);
+
+/*
+ * Enqueue the gradients of one attention forward on `stream`; returns
+ * without waiting.
+ *
+ * For a loss L with dL/d(out) = dout, the proof section (証明) of the formula
+ * page "トランスフォーマーの注意機構" fixes every step: the output display
+ * o = sum_j a_j v_j gives dL/dv_j and dL/da_j = dout . v_j, the Jacobian of
+ * the weights da_j/ds_l = a_j (delta_jl - a_l) gives
+ *     dL/ds_j = a_j (dout . v_j - D),   D = sum_l a_l (dout . v_l) = dout . out,
+ * and the score display s_j = q . k_j / sqrt(d_k) gives
+ *     dq_i = sum_j dL/ds_ij k_j / sqrt(d_k),
+ *     dk_j = sum_i dL/ds_ij q_i / sqrt(d_k),
+ *     dv_j = sum_i a_ij dout_i,
+ * summed over the valid (i, j) pairs of sdpa_forward's masks.
+ *
+ *   q, k, v, B, H, Lq, Lk, d_k, causal, key_lens
+ *            exactly as passed to the sdpa_forward call being differentiated.
+ *   out      [B, H, Lq, d_k], that call's output (handle's dtype).
+ *   lse      [B, H, Lq] float, that call's log-sum-exp (required here): the
+ *            weights are recomputed as a_ij = e^{s_ij - lse_i}.
+ *   dout     [B, H, Lq, d_k], dL/d(out), handle's dtype.
+ *   delta    [B, H, Lq] float, caller-owned, written: D_i = dout_i . out_i
+ *            (fp32).  It is the only intermediate the gradients need and is
+ *            left holding D on return.
+ *   dq       [B, H, Lq, d_k] written (handle's dtype).
+ *   dk, dv   [B, H, Lk, d_k] written (handle's dtype).  Keys that no query
+ *            row sees (past key_lens, or above the causal triangle) get 0;
+ *            so does dq of a row with no valid key.
+ *   stream   HIP stream (hipStream_t) as an opaque pointer; NULL = default.
+ *
+ * Accumulation is fp32 on every path.  bf16: the five products on bf16
+ * matrix cores, the recomputed weights and dL/ds rounded to bf16 (RNE) as
+ * operands; results rounded to bf16 (RNE).  Deterministic: no atomics.
+ *
+ * Errors (returned before anything is enqueued; outputs untouched):
+ * INVALID_VALUE for a NULL handle or pointer (key_lens aside), sizes < 1,
+ * causal not 0/1, element counts overflowing int64, misaligned float
+ * pointers, or any written buffer (delta, dq, dk, dv) overlapping another
+ * argument; NOT_SUPPORTED for d_k outside the handle dtype's range (bf16:
+ * 64 or 128) or bf16 pointers not 16-byte aligned; HIP_ERROR if a launch
+ * fails.
+ */
+sdpa_status_t sdpa_backward(sdpa_handle_t h,
+                            const void* q, const void* k, const void* v,
+                            const void* out, const void* dout, const float* lse,
+                            float* delta, void* dq, void* dk, void* dv,
+                            int B, int H, int Lq, int Lk, int d_k,
+                            int causal, const int32_t* key_lens, void* stream);
 
 /* Release a handle (NULL is accepted).  Does not synchronise any stream. */
 sdpa_status_t sdpa_destroy(sdpa_handle_t h);

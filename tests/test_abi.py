@@ -49,6 +49,8 @@ def test_null_handle_and_pointers_rejected_without_device():
     assert lib.sdpa_create(ctypes.byref(h), 7, 0) == b.INVALID_VALUE
     assert lib.sdpa_destroy(None) == b.SUCCESS
     assert b.sdpa_kernel_name(None, 1, 1, 1, 1, 64, 0, 0) is None
+    assert b.sdpa_backward(None, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                           1, 1, 1, 1, 64, 0, None, None) == b.INVALID_VALUE
 
 
 @pytest.mark.gpu
@@ -84,3 +86,32 @@ def test_validation_statuses_on_gpu():
                           None) == b.NOT_SUPPORTED
     with pytest.raises(b.SdpaError):
         b.forward(x[..., :96].contiguous(), y[..., :96].contiguous(), y[..., :96].contiguous())
+
+
+@pytest.mark.gpu
+def test_backward_validation_statuses_on_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    h = b.handle_for(b.DTYPE_BF16, 0)
+    B, H, L, d = 2, 2, 64, 128
+    t = {n: torch.zeros(B, H, L, d, dtype=torch.bfloat16, device="cuda")
+         for n in ("q", "k", "v", "out", "dout", "dq", "dk", "dv")}
+    lse = torch.zeros(B, H, L, device="cuda")
+    delta = torch.zeros_like(lse)
+    p = lambda x: x.data_ptr()
+    base = dict(handle=h, **{n: p(x) for n, x in t.items()}, lse=p(lse), delta=p(delta),
+                B=B, H=H, Lq=L, Lk=L, d_k=d, causal=0, key_lens=None, stream=None)
+    bwd = lambda **kw: b.sdpa_backward(**{**base, **kw})
+    assert bwd() == b.SUCCESS
+    torch.cuda.synchronize()
+    for name in ("q", "out", "dout", "lse", "delta", "dq", "dk", "dv"):
+        assert bwd(**{name: None}) == b.INVALID_VALUE, name
+    assert bwd(Lq=0) == b.INVALID_VALUE
+    assert bwd(causal=3) == b.INVALID_VALUE
+    assert bwd(dq=p(t["q"])) == b.INVALID_VALUE            # dq aliases q
+    assert bwd(dk=p(t["dv"]) + 512) == b.INVALID_VALUE     # dk overlaps dv
+    assert bwd(delta=p(lse)) == b.INVALID_VALUE            # delta aliases lse
+    assert bwd(d_k=96) == b.NOT_SUPPORTED
+    assert bwd(d_k=64, dv=p(t["dv"]) + 2) == b.NOT_SUPPORTED   # misaligned bf16
+    assert bwd(B=1 << 30, H=1 << 30) == b.INVALID_VALUE

@@ -1,0 +1,163 @@
+"""HIP backward (sdpa_backward) vs the CPU oracle's fp64 gradients, element
+by element, through the C ABI.
+
+The forward runs on the GPU first; its out and lse feed the backward, as in
+training.  Expected values come only from the oracle (oracle.sdpa_bwd).
+
+Tolerances (derivation in the design notes): for bf16, per gradient tensor,
+max |g - r| <= 2e-2 * max |r| and ||g - r||_2 <= 1e-2 * ||r||_2 -- the
+forward's bf16 bar stated relative to the tensor's scale, since gradients
+are not of order 1; for fp32, max |g - r| <= 1e-5 * max(1, max |r|).
+Gradients that the masks make exactly zero (keys no row sees, rows with no
+key) must be exactly zero.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import announce, require_gpu, to_device
+from transformer_scaled_dot_sdpa_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_REL = 2e-2
+BF16_RMS_REL = 1e-2
+F32_MAX = 1e-5
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def run_fwd_bwd(q, k, v, dout, dtype, causal=False, key_lens=None):
+    """Forward then backward on the GPU; returns float32 numpy
+    (dq, dk, dv, delta, out)."""
+    import torch
+    import transformer_scaled_dot_sdpa_amd as sdpa
+    qd, kd, vd, gd = (to_device(x, dtype) for x in (q, k, v, dout))
+    kl = torch.from_numpy(np.asarray(key_lens, dtype=np.int32)).to("cuda") if key_lens is not None else None
+    out, lse = sdpa.forward(qd, kd, vd, causal=causal, key_lens=kl)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = sdpa.backward(qd, kd, vd, out, lse, gd, causal=causal, key_lens=kl, delta=delta)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy()
+    return f(dq), f(dk), f(dv), f(delta), f(out)
+
+
+def oracle_grads(q, k, v, dout, dtype, causal=False, key_lens=None):
+    import oracle
+    return oracle.sdpa_bwd(q, k, v, dout, causal=causal, key_lens=key_lens, bf16=(dtype == "bf16"))
+
+
+def assert_grad_close(g, r, dtype, what):
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    g = g.astype(np.float64)
+    err = np.abs(g - r)
+    scale = float(np.max(np.abs(r))) if r.size else 0.0
+    if dtype == "bf16":
+        if scale == 0.0:
+            assert np.all(g == 0), f"{what}: expected all zeros"
+            return
+        assert err.max() <= BF16_MAX_REL * scale, \
+            f"{what}: max |d| = {err.max():.3g} > {BF16_MAX_REL} * {scale:.3g}"
+        rms = np.linalg.norm(g - r) / np.linalg.norm(r)
+        assert rms <= BF16_RMS_REL, f"{what}: relative rms error {rms:.3g} > {BF16_RMS_REL}"
+    else:
+        bound = F32_MAX * max(1.0, scale)
+        assert err.max() <= bound, f"{what}: max |d| = {err.max():.3g} > {bound:.3g}"
+
+
+def assert_structural_zeros(dq, dk, dv, Lq, Lk, causal, key_lens, what):
+    """Keys no query sees and rows with no key get exactly zero."""
+    B = dq.shape[0]
+    for b in range(B):
+        n = Lk if key_lens is None else min(Lk, max(0, int(key_lens[b])))
+        if causal:
+            n = min(n, Lq)   # key j is seen by rows i >= j only
+        assert np.all(dk[b, :, n:] == 0) and np.all(dv[b, :, n:] == 0), f"{what}: unseen keys b={b}"
+        if n == 0:
+            assert np.all(dq[b] == 0), f"{what}: rows without keys b={b}"
+
+
+def check_case(B, H, Lq, Lk, d, dtype, causal, kl, seed, what):
+    announce(f"backward {what}: B{B} H{H} Lq{Lq} Lk{Lk} d{d} {dtype} causal={causal} "
+             f"key_lens={kl} seed={seed}")
+    q, k, v, _ = inputs.generate(B, H, Lq, Lk, d, dtype, seed)
+    dout = inputs.generate_dout(B, H, Lq, d, dtype, seed)
+    dq, dk, dv, delta, out = run_fwd_bwd(q, k, v, dout, dtype, causal, kl)
+    rq, rk, rv = oracle_grads(q, k, v, dout, dtype, causal, kl)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        assert_grad_close(g, r, dtype, f"{what} {name}")
+    assert_structural_zeros(dq, dk, dv, Lq, Lk, causal, kl, what)
+    # delta is documented as dout . out per row, in fp32
+    g64 = inputs.as_float(dout, dtype).astype(np.float64)
+    prod = g64 * out.astype(np.float64)
+    ref = prod.sum(-1)
+    tol = 1e-5 * np.abs(prod).sum(-1) + 1e-30
+    assert np.all(np.abs(delta - ref) <= tol), f"{what}: delta"
+
+
+CASES = [
+    # B, H, Lq, Lk, causal, key_lens
+    (1, 1, 1, 1, True, None),
+    (1, 1, 7, 7, False, None),
+    (2, 3, 300, 300, True, None),
+    (2, 2, 129, 200, False, [77, 200]),
+    (3, 2, 64, 64, False, [0, 1, 64]),
+    (1, 2, 300, 130, True, None),
+    (1, 2, 100, 333, True, None),
+    (2, 1, 520, 520, True, [300, 520]),
+    (1, 1, 256, 64, False, None),
+]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}q{}k{}c{}L{}".format(*c[:5], c[5]))
+def test_bf16_backward(d, case):
+    B, H, Lq, Lk, causal, kl = case
+    check_case(B, H, Lq, Lk, d, "bf16", causal, kl, 700 + d + Lq + 7 * Lk, f"bf16 d{d} {case}")
+
+
+F32_CASES = [
+    (1, 2, 8, 8, 3, False, None),
+    (1, 2, 8, 8, 3, True, None),
+    (2, 2, 70, 70, 64, True, None),
+    (2, 1, 33, 90, 100, False, [0, 50]),
+    (1, 1, 65, 20, 17, True, None),
+    (1, 1, 20, 65, 256, True, [40]),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "B{}H{}q{}k{}d{}c{}L{}".format(*c))
+def test_f32_backward(case):
+    B, H, Lq, Lk, d, causal, kl = case
+    check_case(B, H, Lq, Lk, d, "fp32", causal, kl, 900 + Lq + 3 * Lk + d, f"fp32 {case}")
+
+
+@pytest.mark.parametrize("name", ["toy_f32", "encoder_d64", "decoder_causal_d64", "cross_padded_d64"])
+def test_backward_named_workload(name):
+    w = inputs.WORKLOADS[name]
+    q, k, v, kl = inputs.generate_workload(w)
+    announce(f"backward {name}: B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} d{w.d} seed={w.seed}")
+    dout = inputs.generate_dout(w.B, w.H, w.Lq, w.d, w.dtype, w.seed)
+    dq, dk, dv, _, _ = run_fwd_bwd(q, k, v, dout, w.dtype, w.causal, kl)
+    rq, rk, rv = oracle_grads(q, k, v, dout, w.dtype, w.causal, kl)
+    for gname, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        assert_grad_close(g, r, w.dtype, f"{name} {gname}")
+    assert_structural_zeros(dq, dk, dv, w.Lq, w.Lk, w.causal, kl, name)
+
+
+def test_backward_large_causal_slices():
+    """The large causal workload at full size in one launch; three whole
+    (batch, head) slices checked against the oracle."""
+    w = inputs.WORKLOADS["large_causal_d128"]
+    announce(f"backward large_causal_d128 full size: generating seed={w.seed}")
+    q, k, v, _ = inputs.generate_workload(w)
+    dout = inputs.generate_dout(w.B, w.H, w.Lq, w.d, w.dtype, w.seed)
+    announce("backward large_causal_d128: running forward + backward")
+    dq, dk, dv, _, _ = run_fwd_bwd(q, k, v, dout, w.dtype, True)
+    for b, h in ((0, 0), (1, 37), (w.B - 1, w.H - 1)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle_grads(q[sl], k[sl], v[sl], dout[sl], w.dtype, True)
+        for gname, g, r in (("dq", dq[sl], rq), ("dk", dk[sl], rk), ("dv", dv[sl], rv)):
+            assert_grad_close(g, r, w.dtype, f"large_causal_d128 b{b} h{h} {gname}")

@@ -1,7 +1,7 @@
 """ctypes binding of the C ABI in ``include/sdpa.h``.
 
 Argument marshalling only: tensors are checked and their device pointers and
-the current HIP stream are passed to ``sdpa_forward``; every step of the
+the current HIP stream are passed to ``sdpa_forward`` / ``sdpa_backward``; every step of the
 computation runs in the library's HIP kernels.  There is no fallback: if the
 library is missing or a call fails, an exception is raised.
 
@@ -21,8 +21,8 @@ SUCCESS, INVALID_VALUE, NOT_SUPPORTED, HIP_ERROR, ALLOC_FAILED = 0, 1, 2, 3, 4
 DTYPE_FP32, DTYPE_BF16 = 0, 1
 
 # Every symbol include/sdpa.h declares.
-EXPORTED = ("sdpa_create", "sdpa_forward", "sdpa_destroy", "sdpa_status_string",
-            "sdpa_kernel_name")
+EXPORTED = ("sdpa_create", "sdpa_forward", "sdpa_backward", "sdpa_destroy",
+            "sdpa_status_string", "sdpa_kernel_name")
 
 
 class SdpaError(RuntimeError):
@@ -54,6 +54,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.sdpa_forward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                          i32, vp, vp]
             lib.sdpa_forward.restype = i32
+            lib.sdpa_backward.argtypes = [vp] * 11 + [i32] * 6 + [vp, vp]
+            lib.sdpa_backward.restype = i32
             lib.sdpa_destroy.argtypes = [vp]
             lib.sdpa_destroy.restype = i32
             lib.sdpa_status_string.argtypes = [i32]
@@ -87,6 +89,14 @@ def sdpa_forward(handle, q, k, v, out, lse, B, H, Lq, Lk, d_k, causal, key_lens,
     """Raw ``sdpa_forward`` on integer pointers; returns the status code."""
     return load_library().sdpa_forward(handle, q, k, v, out, lse, int(B), int(H), int(Lq),
                                        int(Lk), int(d_k), int(causal), key_lens, stream)
+
+
+def sdpa_backward(handle, q, k, v, out, dout, lse, delta, dq, dk, dv, B, H, Lq, Lk, d_k, causal,
+                  key_lens, stream) -> int:
+    """Raw ``sdpa_backward`` on integer pointers; returns the status code."""
+    return load_library().sdpa_backward(handle, q, k, v, out, dout, lse, delta, dq, dk, dv,
+                                        int(B), int(H), int(Lq), int(Lk), int(d_k), int(causal),
+                                        key_lens, stream)
 
 
 def sdpa_kernel_name(handle, B, H, Lq, Lk, d_k, causal, has_key_lens):
@@ -168,6 +178,67 @@ def forward(q, k, v, causal: bool = False, key_lens=None, out=None, lse=None,
     if st != SUCCESS:
         raise SdpaError(st, "sdpa_forward")
     return out, lse
+
+
+def backward(q, k, v, out, lse, dout, causal: bool = False, key_lens=None, dq=None, dk=None,
+             dv=None, delta=None, stream=None):
+    """Gradients (dq, dk, dv) of the forward that produced ``out`` and ``lse``.
+
+    ``q, k, v, causal, key_lens`` as passed to :func:`forward`; ``out`` and
+    ``lse`` its results; ``dout`` the gradient of the loss with respect to
+    ``out`` (q's shape and dtype).  ``dq``/``dk``/``dv`` and the fp32
+    [B, H, Lq] buffer ``delta`` (written with dout . out per row) may be
+    given preallocated.  Returns ``(dq, dk, dv)``.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, L, d_k] tensor")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q's dtype and device")
+    B, H, Lq, d = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have q's shape")
+    Lk = k.shape[2]
+    code = _dtype_code(q)
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+
+    def _vec(t, name):
+        if (not isinstance(t, torch.Tensor) or t.shape != (B, H, Lq) or t.dtype != torch.float32
+                or t.device != q.device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, Lq] tensor on q's device")
+        return t
+
+    _vec(lse, "lse")
+    delta = _vec(delta, "delta") if delta is not None else torch.empty_like(lse)
+    grads = []
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            t = torch.empty_like(ref)
+        elif (t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device
+              or not t.is_contiguous()):
+            raise ValueError(f"{name} must match its input in shape, dtype and device")
+        grads.append(t)
+    dq, dk, dv = grads
+    kl_ptr = None
+    if key_lens is not None:
+        if (key_lens.dtype != torch.int32 or key_lens.shape != (B,) or key_lens.device != q.device
+                or not key_lens.is_contiguous()):
+            raise ValueError("key_lens must be a contiguous int32 [B] tensor on q's device")
+        kl_ptr = key_lens.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = sdpa_backward(handle_for(code, dev), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                       out.data_ptr(), dout.data_ptr(), lse.data_ptr(), delta.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, d,
+                       int(bool(causal)), kl_ptr, stream.cuda_stream)
+    if st != SUCCESS:
+        raise SdpaError(st, "sdpa_backward")
+    return dq, dk, dv
 
 
 def kernel_name(q, k, causal: bool = False, has_key_lens: bool = False):

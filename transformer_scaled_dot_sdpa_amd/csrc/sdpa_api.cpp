@@ -152,4 +152,68 @@ sdpa_status_t sdpa_forward(sdpa_handle_t h, const void* q, const void* k, const 
     return e == hipSuccess ? SDPA_STATUS_SUCCESS : SDPA_STATUS_HIP_ERROR;
 }
 
+sdpa_status_t sdpa_backward(sdpa_handle_t h, const void* q, const void* k, const void* v,
+                            const void* out, const void* dout, const float* lse, float* delta,
+                            void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk, int d_k,
+                            int causal, const int32_t* key_lens, void* stream) {
+    if (h == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr ||
+        dout == nullptr || lse == nullptr || delta == nullptr || dq == nullptr || dk == nullptr ||
+        dv == nullptr)
+        return SDPA_STATUS_INVALID_VALUE;
+    if (B < 1 || H < 1 || Lq < 1 || Lk < 1 || d_k < 1) return SDPA_STATUS_INVALID_VALUE;
+    if (causal != 0 && causal != 1) return SDPA_STATUS_INVALID_VALUE;
+    long long nq = 0, nkv = 0;
+    if (!mul_fits(B, H, Lq, d_k, &nq) || !mul_fits(B, H, Lk, d_k, &nkv))
+        return SDPA_STATUS_INVALID_VALUE;
+    const size_t esz = h->dtype == SDPA_DTYPE_BF16 ? 2 : 4;
+    if ((unsigned long long)nq > SIZE_MAX / esz || (unsigned long long)nkv > SIZE_MAX / esz)
+        return SDPA_STATUS_INVALID_VALUE;
+    const size_t bq = (size_t)nq * esz, bkv = (size_t)nkv * esz;
+    const size_t bl = (size_t)B * H * Lq * sizeof(float);
+    // every written buffer is disjoint from every other buffer
+    struct Span { const void* p; size_t n; };
+    const Span inputs[] = {{q, bq}, {k, bkv}, {v, bkv}, {out, bq}, {dout, bq}, {lse, bl}};
+    const Span outputs[] = {{delta, bl}, {dq, bq}, {dk, bkv}, {dv, bkv}};
+    for (size_t o = 0; o < 4; ++o) {
+        for (const Span& in : inputs)
+            if (overlaps(outputs[o].p, outputs[o].n, in.p, in.n)) return SDPA_STATUS_INVALID_VALUE;
+        for (size_t p = o + 1; p < 4; ++p)
+            if (overlaps(outputs[o].p, outputs[o].n, outputs[p].p, outputs[p].n))
+                return SDPA_STATUS_INVALID_VALUE;
+    }
+    if (reinterpret_cast<uintptr_t>(lse) % alignof(float) != 0 ||
+        reinterpret_cast<uintptr_t>(delta) % alignof(float) != 0)
+        return SDPA_STATUS_INVALID_VALUE;
+    if (key_lens != nullptr && reinterpret_cast<uintptr_t>(key_lens) % alignof(int32_t) != 0)
+        return SDPA_STATUS_INVALID_VALUE;
+    if (h->dtype == SDPA_DTYPE_BF16) {
+        if (d_k != 64 && d_k != 128) return SDPA_STATUS_NOT_SUPPORTED;
+        for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+            if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return SDPA_STATUS_NOT_SUPPORTED;
+    } else {
+        if (d_k > 256) return SDPA_STATUS_NOT_SUPPORTED;
+        for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+            if (reinterpret_cast<uintptr_t>(p) % alignof(float) != 0) return SDPA_STATUS_INVALID_VALUE;
+    }
+
+    sdpa::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.delta = delta;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.key_lens = key_lens;
+    a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk; a.d = d_k; a.causal = causal;
+
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    if (cur != h->device && hipSetDevice(h->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = h->dtype == SDPA_DTYPE_BF16 ? sdpa::launch_bwd_bf16(a, s) : sdpa::launch_bwd_f32(a, s);
+    if (cur != h->device) (void)hipSetDevice(cur);
+    return e == hipSuccess ? SDPA_STATUS_SUCCESS : SDPA_STATUS_HIP_ERROR;
+}
+
 }  // extern "C"

@@ -1,0 +1,549 @@
+// Backward of the fused bf16 attention for gfx950 (CDNA4) matrix cores.
+//
+// For a loss L with dL/dO = dO, and P = softmax(S), S = Q K^T / sqrt(d)
+// (eq. (1) of "Aufmerksamkeit ist alles, was Sie brauchen", section 3.2.1),
+// the proof section (証明) of the formula page "トランスフォーマーの注意機構"
+// gives everything needed:
+//   output display  O = P V          ->  dV = P^T dO,   dP = dO V^T
+//   Jacobian display da_j/ds_l = a_j (delta_jl - a_l)
+//                                    ->  dS = P o (dP - D),  D_i = sum_j P_ij dP_ij
+//                                                               = sum_t dO_it O_it
+//   score display   s = q.k / sqrt(d) ->  dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d)
+// P is recomputed from S and the forward's log-sum-exp (P = exp(S - lse)),
+// so no score matrix is stored.
+//
+// Three kernels:
+//   bwd_delta   D = rowsum(dO o O), one value per query row (fp32);
+//   bwd_dq      per block of 128 query rows (32 per wavefront): stream K and
+//               V tiles of 64 keys through LDS and accumulate
+//               dQ^T += K^T dS^T  after  S^T = K Q^T, dP^T = V dO^T;
+//   bwd_dkdv    per block of 128 keys (32 per wavefront): stream Q and dO
+//               tiles of 64 query rows through LDS and accumulate
+//               dV^T += dO^T P  and  dK^T += Q^T dS  after  S = Q K^T,
+//               dP = dO V^T.
+// All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS
+// are rounded to bf16 (RNE) as MFMA operands.  Every LDS tile uses the
+// forward kernel's K layout (rows permuted by swapping bits 2 and 3 inside
+// each 32-row block, 16-byte chunks XOR-swizzled): read with ds_read_b128 it
+// is the row operand of S / dP, and the permutation puts the result of those
+// products directly in the operand layout of the next one; read with
+// ds_read_b64_tr_b16 it is the transposed operand (K^T, Q^T, dO^T).
+#include "sdpa_internal.h"
+#include "bf16_common.h"
+
+#include <math.h>
+
+namespace sdpa {
+namespace {
+
+using namespace bf16k;
+
+struct BParams {
+    const uint16_t* __restrict__ q;
+    const uint16_t* __restrict__ k;
+    const uint16_t* __restrict__ v;
+    const uint16_t* __restrict__ o;
+    const uint16_t* __restrict__ dout;
+    const float* __restrict__ lse;
+    float* __restrict__ delta;
+    uint16_t* __restrict__ dq;
+    uint16_t* __restrict__ dk;
+    uint16_t* __restrict__ dv;
+    const int32_t* __restrict__ key_lens;
+    int H, Lq, Lk;
+    int num_blocks;    // row blocks per (b, h): query blocks (dq) or key blocks (dkdv)
+    int num_items;
+    int upi;
+    int num_units;
+    float scale;       // 1 / sqrt(d)
+    float scale_log2;  // log2(e) / sqrt(d)
+};
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// ---------------------------------------------------------------- D
+template <int D>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(const uint16_t* __restrict__ o,
+                                                        const uint16_t* __restrict__ dout,
+                                                        float* __restrict__ delta, long long rows) {
+    constexpr int CH = D / 8;                  // 16-byte chunks per row (lanes per row)
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long row = gid / CH;
+    const int c = (int)(gid % CH);
+    float acc = 0.f;
+    if (row < rows) {
+        // a bf16 value widens to fp32 by placing its bits in the high half
+        const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + c * 8);
+        const uint4 g = *reinterpret_cast<const uint4*>(dout + row * D + c * 8);
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(__uint_as_float(aw[e] << 16), __uint_as_float(gw[e] << 16), acc);
+            acc = fmaf(__uint_as_float(aw[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < rows && c == 0) delta[row] = acc;
+}
+
+// Per-lane offsets shared by both kernels (elements inside a 64-row tile in
+// the forward's K layout).
+template <int D>
+struct TileOffsets {
+    static constexpr int NKS = D / 16;
+    static constexpr int NDT = D / 32;
+    int rd[NKS];       // row operand: row n (physical), chunk 2ks + h
+    int tr_lo[NDT];    // transposed operand, logical rows 16s + 8h + 0..3 of a 32-row block
+    int tr_hi[NDT];    // logical rows 16s + 8h + 4..7
+    __device__ __forceinline__ void init(int lane) {
+        const int n = lane & 31, h = lane >> 5, li = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) rd[ks] = n * D + (((2 * ks + h) ^ k_swz<D>(n)) << 3);
+        // logical row 16s + 8h + c sits at physical row 16s + 4h + c (c < 4)
+        // or 16s + 8 + 4h + (c - 4); the swizzle only depends on row bits
+        // below 4, so the 16s and 32-row block offsets are plain additions
+        const int rr = li >> 2;
+        const int colg = 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+        const int plo = 4 * h + rr, phi = 8 + 4 * h + rr;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int col = dt * 32 + colg;
+            tr_lo[dt] = plo * D + (((col >> 3) ^ k_swz<D>(plo)) << 3) + (col & 7);
+            tr_hi[dt] = phi * D + (((col >> 3) ^ k_swz<D>(phi)) << 3) + (col & 7);
+        }
+    }
+};
+
+// transposed operand of rows [32 kt + 16 s, +16) of a tile, output column
+// block dt: lane (n, h) gets rows 16s + 8h + 0..7 (logical) of column
+// 32 dt + n
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const uint16_t* T, const TileOffsets<D>& off, int kt,
+                                          int s, int dt) {
+    const uint16_t* base = T + (32 * kt + 16 * s) * D;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off.tr_lo[dt]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off.tr_hi[dt]));
+    return __builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+// DMA slot offsets of the forward's K layout for this thread's KCH loads
+template <int D, int KCH>
+__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t* boff) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+        const int s = (wave * KCH + u) * 64 + lane;
+        const int row = s / CPR, pc = s % CPR;
+        boff[u] = (k_lds_row(row) * D + ((pc ^ k_swz<D>(row)) << 3)) * 2;
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D, bool CAUSAL, bool LENS>
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BParams p) {
+    constexpr int BC = 64, NT = 256, BR = 128;
+    constexpr int CPR = D / 8;
+    constexpr int KCH = BC * CPR / NT;
+    constexpr int TILE = BC * D;
+    constexpr int NDT = D / 32;
+    constexpr int NKS = D / 16;
+
+    __shared__ __align__(16) uint16_t k_lds0[TILE], k_lds1[TILE], v_lds0[TILE], v_lds1[TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;
+    const int h = lane >> 5;
+    uint32_t boff[KCH];
+    dma_offsets<D, KCH>(wave, lane, boff);
+    TileOffsets<D> off;
+    off.init(lane);
+
+    int unit_first, unit_step, unit_last;
+    workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
+    for (int unit = unit_first; unit < unit_last; unit += unit_step)
+    for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
+    int bh, qb;
+    item_block<CAUSAL>(item, p.num_blocks, &bh, &qb);
+    const int b = bh / p.H;
+    const int q0 = qb * BR;
+    int kv_len = p.Lk;
+    if (LENS) {
+        int L = p.key_lens[b];
+        L = L < 0 ? 0 : L;
+        kv_len = L < kv_len ? L : kv_len;
+    }
+    const int kv_end = CAUSAL ? min(kv_len, q0 + BR) : kv_len;
+    const int ntiles = (kv_end + BC - 1) / BC;
+    const int q0w = q0 + wave * 32;
+    const int qrow = q0w + n;
+    const int wave_kv_end = CAUSAL ? min(kv_len, q0w + 32) : kv_len;
+    const size_t q_base = (size_t)bh * p.Lq * D;
+    const uint16_t* kg = p.k + (size_t)bh * p.Lk * D;
+    const uint16_t* vg = p.v + (size_t)bh * p.Lk * D;
+    const uint32_t kv_bytes = (uint32_t)kv_len * D * 2;
+
+    // Q and dO of the wavefront's rows as B operands (rows past Lq load the
+    // last row; their results are never stored)
+    const int qr = qrow < p.Lq ? qrow : p.Lq - 1;
+    bf16x8 qf[NKS], df[NKS];
+    {
+        const i16x8* sq = reinterpret_cast<const i16x8*>(p.q + q_base + (size_t)qr * D + 8 * h);
+        const i16x8* sd = reinterpret_cast<const i16x8*>(p.dout + q_base + (size_t)qr * D + 8 * h);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            qf[ks] = __builtin_bit_cast(bf16x8, sq[2 * ks]);
+            df[ks] = __builtin_bit_cast(bf16x8, sd[2 * ks]);
+        }
+    }
+    const float lse2 = p.lse[(size_t)bh * p.Lq + qr] * kLog2e;
+    const float dl = p.delta[(size_t)bh * p.Lq + qr];
+    const bool row_ok = qrow < p.Lq;
+
+    auto issue_loads = [&](int t, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
+        const uint32_t toff = (uint32_t)(t * BC) * D * 2;
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            buffer_load_lds16(kg, kv_bytes, (lds_void*)(kb + (wave * KCH + u) * 64 * 8), boff[u], toff);
+            buffer_load_lds16(vg, kv_bytes, (lds_void*)(vb + (wave * KCH + u) * 64 * 8), boff[u], toff);
+        }
+    };
+
+    f32x16 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+
+    auto tile = [&](int t, const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int kbase = t * BC + 32 * kt;
+            if (kbase >= wave_kv_end) continue;
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + off.rd[ks]);
+                const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vs + kt * 32 * D + off.rd[ks]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
+            }
+            // dS^T = P^T o (dP^T - D): accumulator r of lane (n, h) is key
+            // kbase + 16(r/8) + 8h + r%8 of query row n
+            bf16x8 pb[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kbase + 16 * (r >> 3) + 8 * h + (r & 7);
+                bool ok = row_ok && key < kv_len;
+                if (CAUSAL) ok = ok && key <= qrow;
+                const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -lse2)) : 0.f;
+                pb[r >> 3][r & 7] = (__bf16)(pv * (dp[r] - dl));
+            }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Ks, off, kt, st, dt), pb[st],
+                                                                      acc[dt], 0, 0, 0);
+        }
+    };
+
+    if (ntiles > 0) {
+        issue_loads(0, k_lds0, v_lds0);
+        for (int t = 0; t < ntiles; t += 2) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (t + 1 < ntiles) issue_loads(t + 1, k_lds1, v_lds1);
+            tile(t, k_lds0, v_lds0);
+            if (t + 1 >= ntiles) break;
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (t + 2 < ntiles) issue_loads(t + 2, k_lds0, v_lds0);
+            tile(t + 1, k_lds1, v_lds1);
+        }
+    }
+
+    // dQ = (dS K) / sqrt(d): accumulator r of column tile dt is feature
+    // dt*32 + 8*(r/4) + 4h + r%4 of row qrow
+    if (row_ok) {
+        uint16_t* dst = p.dq + q_base + (size_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                __bf16 w[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) w[c] = (__bf16)(acc[dt][4 * g4 + c] * p.scale);
+                *reinterpret_cast<uint2*>(dst + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, w);
+            }
+    }
+    __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D, bool CAUSAL, bool LENS>
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BParams p) {
+    constexpr int BQ = 64, NT = 256, BK = 128;
+    constexpr int CPR = D / 8;
+    constexpr int KCH = BQ * CPR / NT;
+    constexpr int TILE = BQ * D;
+    constexpr int NDT = D / 32;
+    constexpr int NKS = D / 16;
+
+    __shared__ __align__(16) uint16_t q_lds0[TILE], q_lds1[TILE], g_lds0[TILE], g_lds1[TILE];
+    __shared__ __align__(16) float st_lds[2][2][BQ];   // [buffer][lse*log2e, D][row]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;
+    const int h = lane >> 5;
+    uint32_t boff[KCH];
+    dma_offsets<D, KCH>(wave, lane, boff);
+    TileOffsets<D> off;
+    off.init(lane);
+
+    int unit_first, unit_step, unit_last;
+    workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
+    for (int unit = unit_first; unit < unit_last; unit += unit_step)
+    for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
+    int bh, kb;
+    item_block<CAUSAL>(item, p.num_blocks, &bh, &kb);
+    // causal: the lowest key blocks see the most query rows
+    if (CAUSAL) kb = p.num_blocks - 1 - kb;
+    const int b = bh / p.H;
+    const int k0 = kb * BK;
+    int kv_len = p.Lk;
+    if (LENS) {
+        int L = p.key_lens[b];
+        L = L < 0 ? 0 : L;
+        kv_len = L < kv_len ? L : kv_len;
+    }
+    const int k0w = k0 + wave * 32;
+    const int key = k0w + n;
+    // query tiles that can see a key of this block: causal queries i >= k0
+    const int ntq = (p.Lq + BQ - 1) / BQ;
+    const int t0 = CAUSAL ? k0 / BQ : 0;
+    const int t_end = k0 < kv_len ? ntq : t0;   // no valid key in the block: nothing to do
+    const size_t q_base = (size_t)bh * p.Lq * D;
+    const size_t kv_base = (size_t)bh * p.Lk * D;
+    const uint16_t* qg = p.q + q_base;
+    const uint16_t* gg = p.dout + q_base;
+    const uint32_t q_bytes = (uint32_t)p.Lq * D * 2;
+    const float* lse_g = p.lse + (size_t)bh * p.Lq;
+    const float* dl_g = p.delta + (size_t)bh * p.Lq;
+
+    const int kr = key < p.Lk ? key : p.Lk - 1;
+    bf16x8 kf[NKS], vf[NKS];
+    {
+        const i16x8* sk = reinterpret_cast<const i16x8*>(p.k + kv_base + (size_t)kr * D + 8 * h);
+        const i16x8* sv = reinterpret_cast<const i16x8*>(p.v + kv_base + (size_t)kr * D + 8 * h);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            kf[ks] = __builtin_bit_cast(bf16x8, sk[2 * ks]);
+            vf[ks] = __builtin_bit_cast(bf16x8, sv[2 * ks]);
+        }
+    }
+    const bool key_ok = key < kv_len;
+
+    // per-row statistics of a query tile (lse in exp2 units and D), loaded
+    // by the first 128 threads into registers, stored to LDS before the
+    // barrier that opens the tile
+    float stat = 0.f;
+    auto stat_load = [&](int t) __attribute__((always_inline)) {
+        if (tid < 2 * BQ) {
+            int row = t * BQ + (tid & (BQ - 1));
+            row = row < p.Lq ? row : p.Lq - 1;
+            stat = tid < BQ ? lse_g[row] * kLog2e : dl_g[row];
+        }
+    };
+    auto stat_store = [&](int buf) __attribute__((always_inline)) {
+        if (tid < 2 * BQ) st_lds[buf][tid / BQ][tid & (BQ - 1)] = stat;
+    };
+    auto issue_loads = [&](int t, uint16_t* qb, uint16_t* gb) __attribute__((always_inline)) {
+        const uint32_t toff = (uint32_t)(t * BQ) * D * 2;
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            buffer_load_lds16(qg, q_bytes, (lds_void*)(qb + (wave * KCH + u) * 64 * 8), boff[u], toff);
+            buffer_load_lds16(gg, q_bytes, (lds_void*)(gb + (wave * KCH + u) * 64 * 8), boff[u], toff);
+        }
+    };
+
+    f32x16 dka[NDT], dva[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dka[dt][r] = dva[dt][r] = 0.f;
+
+    auto tile = [&](int t, const uint16_t* Qs, const uint16_t* Gs, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            const int qbase = t * BQ + 32 * qt;
+            // causal: rows of this sub-tile all before the wavefront's first key
+            if (CAUSAL && qbase + 31 < k0w) continue;
+            if (qbase >= p.Lq) continue;
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + qt * 32 * D + off.rd[ks]);
+                const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gs + qt * 32 * D + off.rd[ks]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+            }
+            // accumulator r of lane (n, h) is query row qbase + 16(r/8) + 8h +
+            // r%8 against key `key`
+            const float* ls = &st_lds[buf][0][32 * qt];
+            const float* ds_ = &st_lds[buf][1][32 * qt];
+            bf16x8 pb[2], sb[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qi = 16 * (r >> 3) + 8 * h + (r & 7);
+                const int qrow = qbase + qi;
+                bool ok = key_ok && qrow < p.Lq;
+                if (CAUSAL) ok = ok && key <= qrow;
+                const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -ls[qi])) : 0.f;
+                pb[r >> 3][r & 7] = (__bf16)pv;
+                sb[r >> 3][r & 7] = (__bf16)(pv * (dp[r] - ds_[qi]));
+            }
+            // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Gs, off, qt, st, dt), pb[st],
+                                                                      dva[dt], 0, 0, 0);
+                    dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Qs, off, qt, st, dt), sb[st],
+                                                                      dka[dt], 0, 0, 0);
+                }
+        }
+    };
+
+    if (t0 < t_end) {
+        issue_loads(t0, q_lds0, g_lds0);
+        stat_load(t0);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        stat_store(0);
+        for (int t = t0; t < t_end; t += 2) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (t + 1 < t_end) {
+                issue_loads(t + 1, q_lds1, g_lds1);
+                stat_load(t + 1);
+            }
+            tile(t, q_lds0, g_lds0, 0);
+            if (t + 1 >= t_end) break;
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            stat_store(1);
+            __syncthreads();
+            if (t + 2 < t_end) {
+                issue_loads(t + 2, q_lds0, g_lds0);
+                stat_load(t + 2);
+            }
+            tile(t + 1, q_lds1, g_lds1, 1);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            stat_store(0);
+        }
+    }
+
+    // dK = dS^T Q / sqrt(d), dV = P^T dO: accumulator r of column tile dt is
+    // feature dt*32 + 8*(r/4) + 4h + r%4 of key `key`
+    if (key < p.Lk) {
+        uint16_t* dstk = p.dk + kv_base + (size_t)key * D;
+        uint16_t* dstv = p.dv + kv_base + (size_t)key * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                __bf16 wk[4], wv[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    wk[c] = (__bf16)(dka[dt][4 * g4 + c] * p.scale);
+                    wv[c] = (__bf16)dva[dt][4 * g4 + c];
+                }
+                *reinterpret_cast<uint2*>(dstk + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wk);
+                *reinterpret_cast<uint2*>(dstv + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wv);
+            }
+    }
+    __syncthreads();
+    }
+}
+
+template <int D, bool CAUSAL, bool LENS>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+    BParams p;
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.k = static_cast<const uint16_t*>(a.k);
+    p.v = static_cast<const uint16_t*>(a.v);
+    p.o = static_cast<const uint16_t*>(a.out);
+    p.dout = static_cast<const uint16_t*>(a.dout);
+    p.lse = a.lse;
+    p.delta = a.delta;
+    p.dq = static_cast<uint16_t*>(a.dq);
+    p.dk = static_cast<uint16_t*>(a.dk);
+    p.dv = static_cast<uint16_t*>(a.dv);
+    p.key_lens = a.key_lens;
+    p.H = a.H;
+    p.Lq = a.Lq;
+    p.Lk = a.Lk;
+    p.scale = (float)(1.0 / sqrt((double)D));
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+
+    const long long rows = (long long)a.B * a.H * a.Lq;
+    {
+        const long long threads = rows * (D / 8);
+        const long long blocks = (threads + 255) / 256;
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           p.o, p.dout, p.delta, rows);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        p.num_blocks = (a.Lq + 127) / 128;
+        const long long items = (long long)p.num_blocks * a.B * a.H;
+        if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        p.num_items = (int)items;
+        p.upi = CAUSAL ? 2 : 1;
+        p.num_units = (int)((items + p.upi - 1) / p.upi);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, LENS>), dim3((unsigned)p.num_units), dim3(256), 0,
+                           stream, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        p.num_blocks = (a.Lk + 127) / 128;
+        const long long items = (long long)p.num_blocks * a.B * a.H;
+        if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        p.num_items = (int)items;
+        p.upi = CAUSAL ? 2 : 1;
+        p.num_units = (int)((items + p.upi - 1) / p.upi);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, LENS>), dim3((unsigned)p.num_units), dim3(256), 0,
+                           stream, p);
+        return hipGetLastError();
+    }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
+    const bool lens = a.key_lens != nullptr;
+    if (a.causal) return lens ? launch_bwd<D, true, true>(a, s) : launch_bwd<D, true, false>(a, s);
+    return lens ? launch_bwd<D, false, true>(a, s) : launch_bwd<D, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
+    if (a.d == 128) return launch_bwd_d<128>(a, s);
+    if (a.d == 64) return launch_bwd_d<64>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

@@ -21,6 +21,24 @@ struct FwdArgs {
     int num_cus;              // compute units of the device (sizes persistent grids)
 };
 
+// Arguments of the backward kernels.  Layouts as FwdArgs; dout, dq have q's
+// shape, dk, dv k's shape; lse and delta are fp32 [B, H, Lq].
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    float* delta;             // written: D_i = dout_i . out_i
+    void* dq;
+    void* dk;
+    void* dv;
+    const int32_t* key_lens;
+    int B, H, Lq, Lk, d;
+    int causal;
+};
+
 // One bf16 tile configuration.  br = rows of Q per workgroup
 // (32 per wavefront), bc = keys per K/V tile.
 struct Bf16Tile {
@@ -43,5 +61,7 @@ hipError_t launch_fwd_bf16_pipe(const FwdArgs& a, const Bf16Tile& t, hipStream_t
 hipError_t launch_fwd_bf16_pp(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_bf16_wide(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
 
 }  // namespace sdpa

@@ -14,7 +14,10 @@ Recipe (every workload):
 * each is rounded to float32 (round to nearest even) and, for bf16 workloads,
   from float32 to bf16 (round to nearest even); bf16 is kept as uint16 bits;
 * when the workload has padding, ``key_lens = rng.integers(lo, hi,
-  endpoint=True, size=B)`` (int32) is drawn after V.
+  endpoint=True, size=B)`` (int32) is drawn after V;
+* for gradients, the upstream gradient dL/dO comes from a generator of its
+  own, ``PCG64(SeedSequence([seed, 1]))``, iid N(0, 1) of shape
+  ``[B, H, Lq, d]`` (not scaled), rounded the same way.
 
 Large tensors are drawn in chunks from the same generator, which yields the
 same stream as one draw (checked by the test suite).
@@ -128,6 +131,14 @@ def generate(B: int, H: int, Lq: int, Lk: int, d: int, dtype: str, seed: int,
         lo, hi = key_lens
         kl = rng.integers(lo, hi, endpoint=True, size=B).astype(np.int32)
     return q, k, v, kl
+
+
+def generate_dout(B: int, H: int, Lq: int, d: int, dtype: str, seed: int) -> np.ndarray:
+    """Upstream gradient dL/dO for the inputs of ``seed`` (module recipe)."""
+    if dtype not in ("fp32", "bf16"):
+        raise ValueError(dtype)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1])))
+    return _draw(rng, (B, H, Lq, d), 1.0, dtype)
 
 
 def generate_workload(w: Workload):
