@@ -20,6 +20,10 @@ in HBM.  W untimed steps, then K timed steps bracketed by
 * ``cpu_baseline``: the fp64 CPU oracle timed on this host on a bounded
   sample of the same workload (whole (b, h) slices), TFLOP/s by the same
   headline formula;
+* ``backward``: the same workload's ``sdpa_backward`` (gradients dq, dk, dv
+  from dout, out and lse), timed the same way after the forward steps; its
+  algorithmic work is 10*d_k flops per valid pair (five products of 2*d_k:
+  S and dP recomputed once, dV, dQ, dK), reported against the same peak;
 * ``vendor_gemm``: context for the MFMA roofline -- the rate torch.matmul
   (the vendor BLAS) reaches on a large square bf16 product on the same GPU in
   the same run, i.e. what dense matrix cores deliver in practice at the clock
@@ -168,6 +172,50 @@ def vendor_gemm(torch, m: int = 16384, n: int = 16384, k: int = 8192, iters: int
             "kind": f"torch.matmul bf16 ({m}x{k}) by ({k}x{n})", "ms": ms}
 
 
+def backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args, fwd_flops_alg):
+    """Time sdpa_backward on the forward's own outputs (first input set)."""
+    import numpy as np
+    tq, tk, tv, out, lse = sets[0]
+    g = torch.from_numpy(inputs.generate_dout(w.B, w.H, w.Lq, w.d, w.dtype, w.seed))
+    dout = (g.view(torch.bfloat16) if w.dtype == "bf16" else g).cuda()
+    sdpa.forward(tq, tk, tv, causal=w.causal, key_lens=tkl, out=out, lse=lse, stream=stream)
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    delta = torch.empty_like(lse)
+
+    def bstep():
+        sdpa.backward(tq, tk, tv, out, lse, dout, causal=w.causal, key_lens=tkl, dq=dq, dk=dk,
+                      dv=dv, delta=delta, stream=stream)
+
+    steps = max(1, min(args.steps, 20))
+    print(f"[bench] backward: warmup {min(args.warmup, 5)}, timed {steps}", file=sys.stderr,
+          flush=True)
+    for _ in range(min(args.warmup, 5)):
+        bstep()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        bstep()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms_wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    flops = 2.5 * fwd_flops_alg   # 10*d_k per valid pair
+    achieved = flops / (ms * 1e-3) / 1e12
+    head = 2.5 * w.flops / (ms_wall * 1e-3) / 1e12
+    print(f"[bench] backward {ms:.4f} ms/call, {achieved:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    del dq, dk, dv, delta, dout
+    return {"ms_per_call": ms, "ms_per_step_wall": ms_wall, "steps": steps,
+            "value": head, "unit": "TFLOP/s",
+            "flops_note": "10*d_k per pair (2.5x the forward's 4*d_k), halved for causal",
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                         "algorithmic_flops_per_call": flops,
+                         "kernels": "bwd_delta_kernel, bwd_dq_kernel, bwd_dkdv_kernel"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +225,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip the vendor GEMM context measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -290,6 +339,9 @@ def main():
                    "input_scale": w.scale, "seed": w.seed, "input_sets": nsets},
         "roofline": roof,
     }
+    if not args.no_backward and w.dtype == "bf16":
+        result["backward"] = backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args,
+                                          flops_alg)
     if not args.no_vendor_gemm:
         g = vendor_gemm(torch)
         g["attention_value_over_gemm"] = value / g["value"]
