@@ -17,10 +17,11 @@
 //   bwd_dq      per block of 128 query rows (32 per wavefront): stream K and
 //               V tiles of 64 keys through LDS and accumulate
 //               dQ^T += K^T dS^T  after  S^T = K Q^T, dP^T = V dO^T;
-//   bwd_dkdv    per block of 128 keys (32 per pair of wavefronts): stream Q
-//               and dO tiles of 64 query rows through LDS; one wavefront of
-//               the pair accumulates dV^T += dO^T P after S = Q K^T, the
-//               other dK^T += Q^T dS after dP = dO V^T.
+//   bwd_dkdv    per block of 128 keys (32 per wavefront): stream Q and dO
+//               tiles of 64 query rows through LDS and accumulate
+//               dV^T += dO^T P  and  dK^T += Q^T dS  after  S = Q K^T,
+//               dP = dO V^T.  K and V of the wavefront's keys stay in
+//               registers; one wavefront per SIMD holds all four products.
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS
 // are rounded to bf16 (RNE) as MFMA operands.  Every LDS tile has its rows
 // permuted as the forward kernel's K tiles (bits 2 and 3 swapped inside each
@@ -303,15 +304,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-// 8 wavefronts, 128 keys.  Wavefronts w and w + 4 form a pair that owns keys
-// 32 (w % 4) .. + 31 of the block: the first computes S, the weights P and
-// dV^T += dO^T P; the second computes dP and, with P passed through LDS,
-// dS = P o (dP - D) and dK^T += Q^T dS.  Each holds one accumulator and one
-// operand block (K or V), so two wavefronts fit on every SIMD, and the four
-// products are split evenly between them.
 template <int D, bool CAUSAL, bool LENS>
-__global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BParams p) {
-    constexpr int BQ = 64, NT = 512, BK = 128;
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BParams p) {
+    constexpr int BQ = 64, NT = 256, BK = 128;
     constexpr int CPR = D / 8;
     constexpr int KCH = BQ * CPR / NT;
     constexpr int TILE = BQ * D;
@@ -320,17 +315,10 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BParams p) {
 
     __shared__ __align__(16) uint16_t q_lds0[TILE], q_lds1[TILE], g_lds0[TILE], g_lds1[TILE];
     __shared__ __align__(16) float st_lds[2][2][BQ];   // [buffer][lse*log2e, D][row]
-    // P of each pair and sub-tile: 16 values per lane, as four float4 planes.
-    // One array per pair, each smaller than a tile, so that the tiles are
-    // placed first and every tile address fits a read's 16-bit offset field.
-    __shared__ __align__(16) float p_lds0[2 * 4 * 64 * 4], p_lds1[2 * 4 * 64 * 4],
-        p_lds2[2 * 4 * 64 * 4], p_lds3[2 * 4 * 64 * 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = wave & 3;
-    const bool first = wave < 4;   // S, P, dV; otherwise dP, dS, dK
     const int n = lane & 31;
     const int h = lane >> 5;
     uint32_t boff[KCH];
@@ -354,7 +342,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BParams p) {
         L = L < 0 ? 0 : L;
         kv_len = L < kv_len ? L : kv_len;
     }
-    const int k0w = k0 + pair * 32;
+    const int k0w = k0 + wave * 32;
     const int key = k0w + n;
     // query tiles that can see a key of this block: causal queries i >= k0
     const int ntq = (p.Lq + BQ - 1) / BQ;
@@ -368,14 +356,16 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BParams p) {
     const float* lse_g = p.lse + (size_t)bh * p.Lq;
     const float* dl_g = p.delta + (size_t)bh * p.Lq;
 
-    // this wavefront's operand block: K rows (first) or V rows (second)
     const int kr = key < p.Lk ? key : p.Lk - 1;
-    bf16x8 kv[NKS];
+    bf16x8 kf[NKS], vf[NKS];
     {
-        const uint16_t* src = (first ? p.k : p.v) + kv_base + (size_t)kr * D + 8 * h;
-        const i16x8* s8 = reinterpret_cast<const i16x8*>(src);
+        const i16x8* sk = reinterpret_cast<const i16x8*>(p.k + kv_base + (size_t)kr * D + 8 * h);
+        const i16x8* sv = reinterpret_cast<const i16x8*>(p.v + kv_base + (size_t)kr * D + 8 * h);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) kv[ks] = __builtin_bit_cast(bf16x8, s8[2 * ks]);
+        for (int ks = 0; ks < NKS; ++ks) {
+            kf[ks] = __builtin_bit_cast(bf16x8, sk[2 * ks]);
+            vf[ks] = __builtin_bit_cast(bf16x8, sv[2 * ks]);
+        }
     }
     const bool key_ok = key < kv_len;
 
@@ -401,129 +391,74 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BParams p) {
             buffer_load_lds16(gg, q_bytes, (lds_void*)(gb + (wave * KCH + u) * 64 * 8), boff[u], toff);
         }
     };
-    // barrier that leaves the next tile's loads in flight: LDS traffic
-    // (lgkmcnt) drained, vector-memory counter untouched
-    auto mid_barrier = [&]() __attribute__((always_inline)) {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    };
 
-    f32x16 acc[NDT];   // dV^T (first) or dK^T (second)
+    f32x16 dka[NDT], dva[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-
-    float4* my_p = reinterpret_cast<float4*>(pair == 0 ? p_lds0 : pair == 1 ? p_lds1 : pair == 2 ? p_lds2 : p_lds3);
+        for (int r = 0; r < 16; ++r) dka[dt][r] = dva[dt][r] = 0.f;
 
     auto tile = [&](int t, const uint16_t* Qs, const uint16_t* Gs, int buf) __attribute__((always_inline)) {
-        bool live[2];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const int qbase = t * BQ + 32 * qt;
-            // causal: rows of this sub-tile all before the pair's first key
-            live[qt] = qbase < p.Lq && !(CAUSAL && qbase + 31 < k0w);
-        }
-        // S = Q K^T (first) or dP = dO V^T (second); accumulator r of lane
-        // (n, h) is query row qbase + 16(r/8) + 8h + r%8 against key `key`.
-        // Each role runs its own straight-line code with the barrier in the
-        // middle, so their registers never have to coexist.
-        auto product = [&](const uint16_t* As, int qt) __attribute__((always_inline)) {
-            f32x16 x;
+            // causal: rows of this sub-tile all before the wavefront's first key
+            if (CAUSAL && qbase + 31 < k0w) continue;
+            if (qbase >= p.Lq) continue;
+            f32x16 s, dp;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = 0.f;
+            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(As + qt * 32 * D + off.rd[ks]);
-                x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kv[ks], x, 0, 0, 0);
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + qt * 32 * D + off.rd[ks]);
+                const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gs + qt * 32 * D + off.rd[ks]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
             }
-            return x;
-        };
-        if (first) {
-            bf16x8 pb[2][2];
+            // accumulator r of lane (n, h) is query row qbase + 16(r/8) + 8h +
+            // r%8 against key `key`
+            // the row statistics of rows 16j + 8h + 0..7, read as vectors
+            // before any use so that no load sits under a mask
+            float lsv[16], dlv[16];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                if (!live[qt]) continue;
-                f32x16 x = product(Qs, qt);
-                const int qbase = t * BQ + 32 * qt;
-                // lse (exp2 units) of rows 16j + 8h + 0..7, read as vectors
-                // before any use so that no load sits under a mask
-                float lsv[16];
+            for (int j = 0; j < 2; ++j) {
+                const float4* s0 = reinterpret_cast<const float4*>(&st_lds[buf][0][32 * qt + 16 * j + 8 * h]);
+                const float4* s1 = reinterpret_cast<const float4*>(&st_lds[buf][1][32 * qt + 16 * j + 8 * h]);
+                const float4 u0 = s0[0], u1 = s0[1], w0 = s1[0], w1 = s1[1];
+                const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float4* src = reinterpret_cast<const float4*>(&st_lds[buf][0][32 * qt + 16 * j + 8 * h]);
-                    const float4 u0 = src[0], u1 = src[1];
-                    lsv[8 * j + 0] = u0.x; lsv[8 * j + 1] = u0.y; lsv[8 * j + 2] = u0.z; lsv[8 * j + 3] = u0.w;
-                    lsv[8 * j + 4] = u1.x; lsv[8 * j + 5] = u1.y; lsv[8 * j + 6] = u1.z; lsv[8 * j + 7] = u1.w;
+                for (int e = 0; e < 8; ++e) {
+                    lsv[8 * j + e] = uu[e];
+                    dlv[8 * j + e] = ww[e];
                 }
-                // every (row, key) pair of the sub-tile valid: no masking
-                const bool full = qbase + 32 <= p.Lq && k0w + 32 <= kv_len && (!CAUSAL || qbase >= k0w + 31);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qi = 16 * (r >> 3) + 8 * h + (r & 7);
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], p.scale_log2, -lsv[r]));
-                    if (!full) {
-                        bool ok = key_ok && qbase + qi < p.Lq;
-                        if (CAUSAL) ok = ok && key <= qbase + qi;
-                        pv = ok ? pv : 0.f;
-                    }
-                    x[r] = pv;
-                    pb[qt][r >> 3][r & 7] = (__bf16)pv;
-                }
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    my_p[(qt * 4 + c) * 64 + lane] = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
             }
-            mid_barrier();
-            // dV^T += dO^T P
+            // every (row, key) pair of the sub-tile valid: no masking
+            const bool full = qbase + 32 <= p.Lq && k0w + 32 <= kv_len && (!CAUSAL || qbase >= k0w + 31);
+            bf16x8 pb[2], sb[2];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                if (!live[qt]) continue;
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt)
-                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Gs, off, qt, st, dt),
-                                                                          pb[qt][st], acc[dt], 0, 0, 0);
-            }
-        } else {
-            f32x16 x[2];
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-                if (live[qt]) x[qt] = product(Gs, qt);
-            mid_barrier();
-            // dS = P o (dP - D), dK^T += Q^T dS
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                if (!live[qt]) continue;
-                float dv_[16];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float4* src = reinterpret_cast<const float4*>(&st_lds[buf][1][32 * qt + 16 * j + 8 * h]);
-                    const float4 u0 = src[0], u1 = src[1];
-                    dv_[8 * j + 0] = u0.x; dv_[8 * j + 1] = u0.y; dv_[8 * j + 2] = u0.z; dv_[8 * j + 3] = u0.w;
-                    dv_[8 * j + 4] = u1.x; dv_[8 * j + 5] = u1.y; dv_[8 * j + 6] = u1.z; dv_[8 * j + 7] = u1.w;
+            for (int r = 0; r < 16; ++r) {
+                const int qi = 16 * (r >> 3) + 8 * h + (r & 7);
+                const int qrow = qbase + qi;
+                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -lsv[r]));
+                if (!full) {
+                    bool ok = key_ok && qrow < p.Lq;
+                    if (CAUSAL) ok = ok && key <= qrow;
+                    pv = ok ? pv : 0.f;
                 }
-                bf16x8 sb[2];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float4 pv = my_p[(qt * 4 + c) * 64 + lane];
-                    const float pe[4] = {pv.x, pv.y, pv.z, pv.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * c + e;
-                        sb[r >> 3][r & 7] = (__bf16)(pe[e] * (x[qt][r] - dv_[r]));
-                    }
-                }
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt)
-                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Qs, off, qt, st, dt),
-                                                                          sb[st], acc[dt], 0, 0, 0);
+                pb[r >> 3][r & 7] = (__bf16)pv;
+                sb[r >> 3][r & 7] = (__bf16)(pv * (dp[r] - dlv[r]));
             }
+            // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Gs, off, qt, st, dt), pb[st],
+                                                                      dva[dt], 0, 0, 0);
+                    dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Qs, off, qt, st, dt), sb[st],
+                                                                      dka[dt], 0, 0, 0);
+                }
         }
     };
 
@@ -554,19 +489,23 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BParams p) {
         }
     }
 
-    // dK = dS^T Q / sqrt(d) (second), dV = P^T dO (first): accumulator r of
-    // column tile dt is feature dt*32 + 8*(r/4) + 4h + r%4 of key `key`
+    // dK = dS^T Q / sqrt(d), dV = P^T dO: accumulator r of column tile dt is
+    // feature dt*32 + 8*(r/4) + 4h + r%4 of key `key`
     if (key < p.Lk) {
-        uint16_t* dst = (first ? p.dv : p.dk) + kv_base + (size_t)key * D;
-        const float sc = first ? 1.f : p.scale;
+        uint16_t* dstk = p.dk + kv_base + (size_t)key * D;
+        uint16_t* dstv = p.dv + kv_base + (size_t)key * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                __bf16 w[4];
+                __bf16 wk[4], wv[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) w[c] = (__bf16)(acc[dt][4 * g4 + c] * sc);
-                *reinterpret_cast<uint2*>(dst + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, w);
+                for (int c = 0; c < 4; ++c) {
+                    wk[c] = (__bf16)(dka[dt][4 * g4 + c] * p.scale);
+                    wv[c] = (__bf16)dva[dt][4 * g4 + c];
+                }
+                *reinterpret_cast<uint2*>(dstk + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wk);
+                *reinterpret_cast<uint2*>(dstv + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wv);
             }
     }
     __syncthreads();
@@ -622,7 +561,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         p.num_items = (int)items;
         p.upi = CAUSAL ? 2 : 1;
         p.num_units = (int)((items + p.upi - 1) / p.upi);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, LENS>), dim3((unsigned)p.num_units), dim3(512), 0,
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, LENS>), dim3((unsigned)p.num_units), dim3(256), 0,
                            stream, p);
         return hipGetLastError();
     }
