@@ -24,6 +24,10 @@ in HBM.  W untimed steps, then K timed steps bracketed by
   from dout, out and lse), timed the same way after the forward steps; its
   algorithmic work is 10*d_k flops per valid pair (five products of 2*d_k:
   S and dP recomputed once, dV, dQ, dK), reported against the same peak;
+* ``decode``: ``sdpa_decode`` (1..8 query rows, split over key chunks) on a
+  decode-shaped workload (default ``decode_d128``), timed with HIP events,
+  reported as HBM GB/s of algorithmic bytes (the workload is bandwidth
+  bound), with ``sdpa_forward`` timed on the same inputs beside it;
 * ``vendor_gemm``: context for the MFMA roofline -- the rate torch.matmul
   (the vendor BLAS) reaches on a large square bf16 product on the same GPU in
   the same run, i.e. what dense matrix cores deliver in practice at the clock
@@ -216,6 +220,57 @@ def backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args, fwd_flops_alg)
                          "kernels": "bwd_delta_kernel, bwd_dq_kernel, bwd_dkdv_kernel"}}
 
 
+def decode_leg(torch, sdpa, inputs, name, args):
+    """Time sdpa_decode and, on the same inputs, sdpa_forward."""
+    import numpy as np
+    w = inputs.WORKLOADS[name]
+    print(f"[bench] decode leg: generating {w.name} (seed {w.seed})", file=sys.stderr, flush=True)
+    q, k, v, kl = inputs.generate_workload(w)
+    up = lambda x: torch.from_numpy(x).view(torch.bfloat16).cuda()
+    tq, tk, tv = up(q), up(k), up(v)
+    tkl = torch.from_numpy(kl).cuda() if kl is not None else None
+    _, bytes_alg = algorithmic_work(w, kl)
+    set_bytes = (tq.numel() + tk.numel() + tv.numel()) * 2
+    nsets = 1 if set_bytes >= (1 << 30) else int(math.ceil((1 << 30) / set_bytes))
+    sets = [(tq, tk, tv)] + [(tq.clone(), tk.clone(), tv.clone()) for _ in range(nsets - 1)]
+    out = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
+    need = sdpa.decode_workspace_size(tq, tk)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps):
+        for i in range(min(args.warmup, 5)):
+            fn(sets[i % nsets])
+        torch.cuda.synchronize()
+        st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            st[i].record(stream)
+            fn(sets[i % nsets])
+            en[i].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in zip(st, en)]))
+
+    steps = max(1, min(args.steps, 50))
+    dec_ms = timed(lambda a: sdpa.decode(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=out,
+                                         lse=lse, workspace=ws, stream=stream), steps)
+    fwd_ms = timed(lambda a: sdpa.forward(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=out,
+                                          lse=lse, stream=stream), steps)
+    gbs = bytes_alg / (dec_ms * 1e-3) / 1e9
+    print(f"[bench] decode {w.name}: {dec_ms*1e3:.1f} us ({gbs:.0f} GB/s); forward on the same "
+          f"inputs {fwd_ms*1e3:.1f} us", file=sys.stderr, flush=True)
+    del sets, out, lse, ws
+    return {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d_k": w.d,
+            "key_lens": None if kl is None else "uniform[%d,%d]" % w.key_lens,
+            "input_sets": nsets, "steps": steps, "us_per_call": dec_ms * 1e3,
+            "workspace_bytes": need,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_call": bytes_alg,
+                         "kernels": "decode_kernel (+ decode_combine when split)"},
+            "forward_same_inputs_us": fwd_ms * 1e3}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +281,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--decode-workload", default="decode_d128",
+                    help="decode-shaped workload of the decode leg ('none' skips it)")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip the vendor GEMM context measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -342,6 +399,8 @@ def main():
     if not args.no_backward and w.dtype == "bf16":
         result["backward"] = backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args,
                                           flops_alg)
+    if args.decode_workload != "none":
+        result["decode"] = decode_leg(torch, sdpa, inputs, args.decode_workload, args)
     if not args.no_vendor_gemm:
         g = vendor_gemm(torch)
         g["attention_value_over_gemm"] = value / g["value"]

@@ -25,6 +25,7 @@
 #ifndef SDPA_MI355X_H_
 #define SDPA_MI355X_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -148,6 +149,45 @@ sdpa_status_t sdpa_backward(sdpa_handle_t h,
                             float* delta, void* dq, void* dk, void* dv,
                             int B, int H, int Lq, int Lk, int d_k,
                             int causal, const int32_t* key_lens, void* stream);
+
+/*
+ * Decode-shaped forward: the same operation, masks and outputs as
+ * sdpa_forward, for a few query rows (1 <= Lq <= 8) against a long key/value
+ * sequence -- the shape of generating one position per step (cookipedia
+ * article, section "全体").  bf16 handles, d_k in {64, 128}.  For the usual
+ * decode step (the newest position attends to every cached key) pass
+ * causal = 0 and the context length per batch in key_lens; causal = 1 keeps
+ * sdpa_forward's top-left meaning.
+ *
+ * Each (b, h) slice is split into key chunks so that few slices still fill
+ * the GPU; each chunk yields a partial output and log-sum-exp, merged as
+ * lse = ln sum_c e^{lse_c}, out = sum_c e^{lse_c - lse} out_c (the ratio
+ * identity of the formula page "トランスフォーマーの注意機構", section 証明,
+ * with the log-sum-exp of section 広がる学問).  The partial results live in
+ * a caller-owned workspace:
+ *   workspace        device memory of at least workspace_bytes, 4-byte
+ *                    aligned, not overlapping any other argument; contents
+ *                    on entry are ignored and on return unspecified.  May be
+ *                    NULL when sdpa_decode_workspace_size returns 0.
+ *   workspace_bytes  its size; must be >= sdpa_decode_workspace_size(...)
+ *                    for the same arguments.
+ * Other arguments as sdpa_forward.  Errors: as sdpa_forward, plus
+ * INVALID_VALUE for a missing, short, misaligned or overlapping workspace and
+ * NOT_SUPPORTED for fp32 handles, Lq > 8 or d_k outside {64, 128}.
+ */
+sdpa_status_t sdpa_decode(sdpa_handle_t h,
+                          const void* q, const void* k, const void* v,
+                          void* out, float* lse,
+                          int B, int H, int Lq, int Lk, int d_k,
+                          int causal, const int32_t* key_lens,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace sdpa_decode needs for these sizes on this handle's
+ * device (0: none needed, or the combination is not supported).  Depends
+ * only on the arguments and the device's compute-unit count.
+ */
+size_t sdpa_decode_workspace_size(sdpa_handle_t h, int B, int H, int Lq, int Lk, int d_k);
 
 /* Release a handle (NULL is accepted).  Does not synchronise any stream. */
 sdpa_status_t sdpa_destroy(sdpa_handle_t h);

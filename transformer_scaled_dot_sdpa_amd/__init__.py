@@ -5,7 +5,8 @@ softmax(q k^T / sqrt(d_k)) v for every (batch, head) slice in the library's
 HIP kernels (see ``include/sdpa.h`` for the C ABI).  The shared library is
 loaded on first use; ``python -m transformer_scaled_dot_sdpa_amd.build``
 builds it.  ``backward(q, k, v, out, lse, dout, ...)`` returns the gradients
-(dq, dk, dv) of that forward, also in HIP kernels.
+(dq, dk, dv) of that forward, also in HIP kernels; ``decode(q, k, v, ...)``
+is the forward for 1..8 query rows, split over key chunks.
 """
-from .binding import (SdpaError, backward, forward, kernel_name, load_library,  # noqa: F401
-                      LIB_PATH, EXPORTED)
+from .binding import (SdpaError, backward, decode, decode_workspace_size, forward,  # noqa: F401
+                      kernel_name, load_library, LIB_PATH, EXPORTED)

@@ -21,8 +21,9 @@ SUCCESS, INVALID_VALUE, NOT_SUPPORTED, HIP_ERROR, ALLOC_FAILED = 0, 1, 2, 3, 4
 DTYPE_FP32, DTYPE_BF16 = 0, 1
 
 # Every symbol include/sdpa.h declares.
-EXPORTED = ("sdpa_create", "sdpa_forward", "sdpa_backward", "sdpa_destroy",
-            "sdpa_status_string", "sdpa_kernel_name")
+EXPORTED = ("sdpa_create", "sdpa_forward", "sdpa_backward", "sdpa_decode",
+            "sdpa_decode_workspace_size", "sdpa_destroy", "sdpa_status_string",
+            "sdpa_kernel_name")
 
 
 class SdpaError(RuntimeError):
@@ -56,6 +57,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.sdpa_forward.restype = i32
             lib.sdpa_backward.argtypes = [vp] * 11 + [i32] * 6 + [vp, vp]
             lib.sdpa_backward.restype = i32
+            lib.sdpa_decode.argtypes = [vp] * 6 + [i32] * 6 + [vp, vp, ctypes.c_size_t, vp]
+            lib.sdpa_decode.restype = i32
+            lib.sdpa_decode_workspace_size.argtypes = [vp] + [i32] * 5
+            lib.sdpa_decode_workspace_size.restype = ctypes.c_size_t
             lib.sdpa_destroy.argtypes = [vp]
             lib.sdpa_destroy.restype = i32
             lib.sdpa_status_string.argtypes = [i32]
@@ -97,6 +102,19 @@ def sdpa_backward(handle, q, k, v, out, dout, lse, delta, dq, dk, dv, B, H, Lq, 
     return load_library().sdpa_backward(handle, q, k, v, out, dout, lse, delta, dq, dk, dv,
                                         int(B), int(H), int(Lq), int(Lk), int(d_k), int(causal),
                                         key_lens, stream)
+
+
+def sdpa_decode(handle, q, k, v, out, lse, B, H, Lq, Lk, d_k, causal, key_lens, workspace,
+                workspace_bytes, stream) -> int:
+    """Raw ``sdpa_decode`` on integer pointers; returns the status code."""
+    return load_library().sdpa_decode(handle, q, k, v, out, lse, int(B), int(H), int(Lq), int(Lk),
+                                      int(d_k), int(causal), key_lens, workspace,
+                                      int(workspace_bytes), stream)
+
+
+def sdpa_decode_workspace_size(handle, B, H, Lq, Lk, d_k) -> int:
+    return int(load_library().sdpa_decode_workspace_size(handle, int(B), int(H), int(Lq),
+                                                         int(Lk), int(d_k)))
 
 
 def sdpa_kernel_name(handle, B, H, Lq, Lk, d_k, causal, has_key_lens):
@@ -239,6 +257,66 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, key_lens=None, dq=No
     if st != SUCCESS:
         raise SdpaError(st, "sdpa_backward")
     return dq, dk, dv
+
+
+def decode(q, k, v, causal: bool = False, key_lens=None, out=None, lse=None,
+           need_lse: bool = True, workspace=None, stream=None):
+    """Decode-shaped forward (1 <= Lq <= 8 query rows, bf16, d_k 64 or 128):
+    the same result as :func:`forward`, split over key chunks.  ``workspace``
+    may be a preallocated uint8 CUDA tensor of at least
+    ``decode_workspace_size(...)`` bytes; otherwise one is allocated here.
+    Returns ``(out, lse)``."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, L, d_k] tensor")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q's dtype and device")
+    B, H, Lq, d = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    Lk = k.shape[2]
+    code = _dtype_code(q)
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    h = handle_for(code, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must match q in shape, dtype and device, and be contiguous")
+    if lse is None and need_lse:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, Lq) or lse.dtype != torch.float32
+                            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be float32 [B, H, Lq] on q's device")
+    kl_ptr = None
+    if key_lens is not None:
+        if (key_lens.dtype != torch.int32 or key_lens.shape != (B,) or key_lens.device != q.device
+                or not key_lens.is_contiguous()):
+            raise ValueError("key_lens must be a contiguous int32 [B] tensor on q's device")
+        kl_ptr = key_lens.data_ptr()
+    need = sdpa_decode_workspace_size(h, B, H, Lq, Lk, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = sdpa_decode(h, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                     lse.data_ptr() if lse is not None else None, B, H, Lq, Lk, d,
+                     int(bool(causal)), kl_ptr, ws_ptr, ws_bytes, stream.cuda_stream)
+    if st != SUCCESS:
+        raise SdpaError(st, "sdpa_decode")
+    return out, lse
+
+
+def decode_workspace_size(q, k) -> int:
+    """Workspace bytes :func:`decode` needs for these tensors."""
+    import torch
+    B, H, Lq, d = q.shape
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    return sdpa_decode_workspace_size(handle_for(_dtype_code(q), dev), B, H, Lq, k.shape[2], d)
 
 
 def kernel_name(q, k, causal: bool = False, has_key_lens: bool = False):

@@ -1,5 +1,6 @@
-// C ABI of the attention forward (declared in include/sdpa.h): handle
-// management, argument validation and dispatch to the HIP kernels.
+// C ABI of the attention forward, decode forward and backward (declared in
+// include/sdpa.h): handle management, argument validation and dispatch to
+// the HIP kernels.
 #include "sdpa.h"
 
 #include <hip/hip_runtime.h>
@@ -212,6 +213,74 @@ sdpa_status_t sdpa_backward(sdpa_handle_t h, const void* q, const void* k, const
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = h->dtype == SDPA_DTYPE_BF16 ? sdpa::launch_bwd_bf16(a, s) : sdpa::launch_bwd_f32(a, s);
+    if (cur != h->device) (void)hipSetDevice(cur);
+    return e == hipSuccess ? SDPA_STATUS_SUCCESS : SDPA_STATUS_HIP_ERROR;
+}
+
+size_t sdpa_decode_workspace_size(sdpa_handle_t h, int B, int H, int Lq, int Lk, int d_k) {
+    if (h == nullptr || B < 1 || H < 1 || Lq < 1 || Lk < 1 || d_k < 1) return 0;
+    if (h->dtype != SDPA_DTYPE_BF16 || (d_k != 64 && d_k != 128) || Lq > sdpa::kDecodeMaxLq) return 0;
+    long long n = 0;
+    if (!mul_fits(B, H, Lq, d_k, &n) || !mul_fits(B, H, Lk, d_k, &n)) return 0;
+    return sdpa::plan_decode(B, H, Lq, Lk, d_k, h->num_cus).workspace_bytes;
+}
+
+sdpa_status_t sdpa_decode(sdpa_handle_t h, const void* q, const void* k, const void* v, void* out,
+                          float* lse, int B, int H, int Lq, int Lk, int d_k, int causal,
+                          const int32_t* key_lens, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (h == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+        return SDPA_STATUS_INVALID_VALUE;
+    if (B < 1 || H < 1 || Lq < 1 || Lk < 1 || d_k < 1) return SDPA_STATUS_INVALID_VALUE;
+    if (causal != 0 && causal != 1) return SDPA_STATUS_INVALID_VALUE;
+    if (h->dtype != SDPA_DTYPE_BF16 || (d_k != 64 && d_k != 128) || Lq > sdpa::kDecodeMaxLq)
+        return SDPA_STATUS_NOT_SUPPORTED;
+    long long nq = 0, nkv = 0;
+    if (!mul_fits(B, H, Lq, d_k, &nq) || !mul_fits(B, H, Lk, d_k, &nkv))
+        return SDPA_STATUS_INVALID_VALUE;
+    if ((unsigned long long)nkv > SIZE_MAX / 2) return SDPA_STATUS_INVALID_VALUE;
+    const size_t bq = (size_t)nq * 2, bkv = (size_t)nkv * 2;
+    const size_t bl = (size_t)B * H * Lq * sizeof(float);
+    const sdpa::DecodePlan plan = sdpa::plan_decode(B, H, Lq, Lk, d_k, h->num_cus);
+    if (plan.workspace_bytes > 0) {
+        if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return SDPA_STATUS_INVALID_VALUE;
+        if (reinterpret_cast<uintptr_t>(workspace) % alignof(float) != 0) return SDPA_STATUS_INVALID_VALUE;
+    }
+    struct Span { const void* p; size_t n; };
+    const Span inputs[] = {{q, bq}, {k, bkv}, {v, bkv}};
+    const Span outputs[] = {{out, bq}, {lse, lse ? bl : 0},
+                            {workspace, plan.workspace_bytes}};
+    for (size_t o = 0; o < 3; ++o) {
+        if (outputs[o].p == nullptr || outputs[o].n == 0) continue;
+        for (const Span& in : inputs)
+            if (overlaps(outputs[o].p, outputs[o].n, in.p, in.n)) return SDPA_STATUS_INVALID_VALUE;
+        for (size_t p2 = o + 1; p2 < 3; ++p2)
+            if (outputs[p2].p != nullptr && outputs[p2].n != 0 &&
+                overlaps(outputs[o].p, outputs[o].n, outputs[p2].p, outputs[p2].n))
+                return SDPA_STATUS_INVALID_VALUE;
+    }
+    if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % alignof(float) != 0)
+        return SDPA_STATUS_INVALID_VALUE;
+    if (key_lens != nullptr && reinterpret_cast<uintptr_t>(key_lens) % alignof(int32_t) != 0)
+        return SDPA_STATUS_INVALID_VALUE;
+    for (const void* p : {q, k, v, (const void*)out})
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return SDPA_STATUS_NOT_SUPPORTED;
+
+    sdpa::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.key_lens = key_lens;
+    a.workspace = workspace;
+    a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk; a.d = d_k; a.causal = causal;
+
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    if (cur != h->device && hipSetDevice(h->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    hipError_t e = sdpa::launch_decode_bf16(a, plan, static_cast<hipStream_t>(stream));
     if (cur != h->device) (void)hipSetDevice(cur);
     return e == hipSuccess ? SDPA_STATUS_SUCCESS : SDPA_STATUS_HIP_ERROR;
 }

@@ -1,0 +1,364 @@
+// Decode-shaped attention forward in bf16: a few query rows (1..8) against a
+// long key/value sequence, the form of generating one token per step
+// (cookipedia article, "全体": the decoder produces the output one position
+// at a time).  Same operation and masks as the main forward
+// (softmax(Q K^T / sqrt(d)) V, "Aufmerksamkeit ist alles, was Sie
+// brauchen", section 3.2.1, eq. (1)).
+//
+// Work of this shape reads every key and value row once and does 4*d flops
+// per row and query, so it is bound by HBM bandwidth; a matrix-core product
+// would waste 31 of its 32 rows.  The kernel therefore uses the vector ALU:
+//
+// * Each (b, h) slice is split into key chunks so that the grid covers the
+//   GPU even for a handful of slices.  One workgroup (4 wavefronts) takes one
+//   chunk; its wavefronts stream interleaved groups of rows with 16-byte
+//   loads, each row spread over d/8 lanes (a 64-lane load reads 1 KiB of
+//   consecutive rows).
+// * Per query row and wavefront: running maximum m (wave-uniform), and per
+//   lane group a running sum l and output slice o, rescaled by 2^(m_old -
+//   m_new) when m grows -- exact by the ratio identity of the formula page
+//   "トランスフォーマーの注意機構", section 証明.
+// * The four wavefronts' (m, l, o) are merged in LDS.  With one chunk the
+//   result is written as out/lse directly; otherwise the chunk's normalised
+//   o and natural-log lse go to the workspace and decode_combine merges the
+//   chunks: lse = ln sum_c e^{lse_c}, o = sum_c e^{lse_c - lse} o_c, the
+//   same identity with the log-sum-exp of section 広がる学問.
+#include "sdpa_internal.h"
+
+#include <math.h>
+
+namespace sdpa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+struct DParams {
+    const uint16_t* __restrict__ q;
+    const uint16_t* __restrict__ k;
+    const uint16_t* __restrict__ v;
+    uint16_t* __restrict__ out;
+    float* __restrict__ lse;          // may be null
+    const int32_t* __restrict__ key_lens;
+    float* __restrict__ part_o;       // [splits][B*H*Lq][d] (splits > 1)
+    float* __restrict__ part_lse;     // [splits][B*H*Lq]
+    int H, Lq, Lk;
+    int causal;
+    int splits;
+    int chunk;                        // keys per split (multiple of the step)
+    float scale_log2;                 // log2(e) / sqrt(d)
+};
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    const __bf16 b = (__bf16)x;   // round to nearest even
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// Sum over the lanes of one row group (CPR consecutive lanes).
+template <int CPR>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < CPR; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+}
+// Maximum / sum over the row groups of a wavefront (lanes l, l ^ CPR, ...).
+template <int CPR>
+__device__ __forceinline__ float across_groups_max(float x) {
+#pragma unroll
+    for (int off = CPR; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+template <int CPR>
+__device__ __forceinline__ float across_groups_sum(float x) {
+#pragma unroll
+    for (int off = CPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+template <int D, int NQ>
+__global__ void __launch_bounds__(kThreads) decode_kernel(DParams p) {
+    constexpr int CPR = D / 8;          // lanes per key row (16 bytes each)
+    constexpr int G = 64 / CPR;         // key rows per wavefront step
+    constexpr int STEP = G * kWaves;    // key rows per workgroup step
+    constexpr int UNROLL = 4;
+
+    __shared__ float red_m[kWaves][NQ], red_l[kWaves][NQ];
+    __shared__ float red_o[kWaves][NQ][D];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane / CPR;         // key row of this lane inside a step
+    const int c = lane % CPR;           // 16-byte chunk (features 8c .. 8c + 7)
+
+    const int split = blockIdx.x % p.splits;
+    const int bh = blockIdx.x / p.splits;
+    const int b = bh / p.H;
+    int kv_len = p.Lk;
+    if (p.key_lens != nullptr) {
+        int L = p.key_lens[b];
+        L = L < 0 ? 0 : L;
+        kv_len = L < kv_len ? L : kv_len;
+    }
+    const int k_lo = split * p.chunk;
+    const int k_hi = min(k_lo + p.chunk, kv_len);
+
+    // query rows (pre-scaled into exp2 units) and their valid key bounds
+    float qv[NQ][8];
+    int n_valid[NQ];
+    const size_t q_row0 = (size_t)bh * p.Lq;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int ii = i < p.Lq ? i : p.Lq - 1;
+        const uint4 w = *reinterpret_cast<const uint4*>(p.q + (q_row0 + ii) * D + 8 * c);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qv[i][2 * e] = bf_lo(ww[e]) * p.scale_log2;
+            qv[i][2 * e + 1] = bf_hi(ww[e]) * p.scale_log2;
+        }
+        int n = k_hi;
+        if (p.causal) n = min(n, i + 1);
+        n_valid[i] = i < p.Lq ? n : k_lo;   // rows past Lq see nothing
+    }
+
+    float m[NQ], l[NQ], o[NQ][8];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        m[i] = -INFINITY;
+        l[i] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[i][e] = 0.f;
+    }
+
+    const uint16_t* kb = p.k + (size_t)bh * p.Lk * D;
+    const uint16_t* vb = p.v + (size_t)bh * p.Lk * D;
+    // this lane's row in step s: k_lo + s * STEP + wave * G + grp
+    const int row0 = k_lo + wave * G + grp;
+
+    auto consume = [&](int row, uint4 kw, uint4 vw) __attribute__((always_inline)) {
+        const uint32_t ka[4] = {kw.x, kw.y, kw.z, kw.w};
+        const uint32_t va[4] = {vw.x, vw.y, vw.z, vw.w};
+        float kf[8], vf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kf[2 * e] = bf_lo(ka[e]);
+            kf[2 * e + 1] = bf_hi(ka[e]);
+            vf[2 * e] = bf_lo(va[e]);
+            vf[2 * e + 1] = bf_hi(va[e]);
+        }
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            float z = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z = fmaf(qv[i][e], kf[e], z);
+            z = group_sum<CPR>(z);
+            const bool ok = row < n_valid[i];
+            const float s = ok ? z : -INFINITY;
+            const float mn = fmaxf(m[i], across_groups_max<CPR>(s));
+            if (mn == -INFINITY) continue;   // wave-uniform: nothing valid yet
+            const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);   // 0 when m was -inf
+            const float pj = ok ? __builtin_amdgcn_exp2f(z - mn) : 0.f;
+            l[i] = fmaf(l[i], alpha, pj);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[i][e] = fmaf(o[i][e], alpha, pj * vf[e]);
+            m[i] = mn;
+        }
+    };
+
+    // a lane whose row is at or past k_hi loads row k_lo instead (in
+    // bounds, and a row of this chunk) and masks it
+    const int nsteps = (k_hi - k_lo + STEP - 1) / STEP;
+    int s = 0;
+    for (; s + UNROLL <= nsteps; s += UNROLL) {
+        uint4 kw[UNROLL], vw[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int row = row0 + (s + u) * STEP;
+            const int rr = row < k_hi ? row : k_lo;
+            kw[u] = *reinterpret_cast<const uint4*>(kb + (size_t)rr * D + 8 * c);
+            vw[u] = *reinterpret_cast<const uint4*>(vb + (size_t)rr * D + 8 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) consume(row0 + (s + u) * STEP, kw[u], vw[u]);
+    }
+    for (; s < nsteps; ++s) {
+        const int row = row0 + s * STEP;
+        const int rr = row < k_hi ? row : k_lo;
+        const uint4 kw = *reinterpret_cast<const uint4*>(kb + (size_t)rr * D + 8 * c);
+        const uint4 vw = *reinterpret_cast<const uint4*>(vb + (size_t)rr * D + 8 * c);
+        consume(row, kw, vw);
+    }
+
+    // merge the row groups of the wavefront (same m), then the wavefronts
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        l[i] = across_groups_sum<CPR>(l[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[i][e] = across_groups_sum<CPR>(o[i][e]);
+        if (lane < CPR) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red_o[wave][i][8 * c + e] = o[i][e];
+        }
+        if (lane == 0) {
+            red_m[wave][i] = m[i];
+            red_l[wave][i] = l[i];
+        }
+    }
+    __syncthreads();
+
+    // thread t merges feature t % D of row t / D
+    for (int t = threadIdx.x; t < NQ * D; t += kThreads) {
+        const int i = t / D, f = t % D;
+        if (i >= p.Lq) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][i]);
+        float L = 0.f, O = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float sc = __builtin_amdgcn_exp2f(red_m[w][i] - M);   // 0 for an empty wavefront
+                L = fmaf(red_l[w][i], sc, L);
+                O = fmaf(red_o[w][i][f], sc, O);
+            }
+        }
+        const size_t row = q_row0 + i;
+        const float on = L > 0.f ? O / L : 0.f;
+        const float ls = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+        if (p.splits == 1) {
+            p.out[row * D + f] = to_bf16(on);
+            if (p.lse != nullptr && f == 0) p.lse[row] = ls;
+        } else {
+            const size_t rows = (size_t)gridDim.x / p.splits * p.Lq;
+            p.part_o[((size_t)split * rows + row) * D + f] = on;
+            if (f == 0) p.part_lse[(size_t)split * rows + row] = ls;
+        }
+    }
+}
+
+// One wavefront per output row: lse = ln sum_c e^{lse_c}, o = sum_c
+// e^{lse_c - lse} o_c over the chunks; a row with no valid key in any chunk
+// gets o = 0, lse = -inf.  Lane c handles chunk c (64 at a time) for the
+// weights, which then go through LDS to the feature loop, whose loads are
+// independent of each other.
+template <int D>
+__global__ void __launch_bounds__(256) decode_combine(DParams p, long long rows) {
+    __shared__ float wsh[4][64];
+    const int wave = threadIdx.x >> 6;
+    const long long row = (long long)blockIdx.x * 4 + wave;
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;   // wave-uniform; no block-wide barrier below
+    float M = -INFINITY;
+    for (int c0 = 0; c0 < p.splits; c0 += 64) {
+        const int c = c0 + lane;
+        const float x = c < p.splits ? p.part_lse[(size_t)c * rows + row] : -INFINITY;
+        M = fmaxf(M, x);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float acc[D / 64];
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) acc[r] = 0.f;
+    float Z = 0.f;
+    if (M != -INFINITY) {
+        for (int c0 = 0; c0 < p.splits; c0 += 64) {
+            const int c = c0 + lane;
+            const float wc = c < p.splits ? __expf(p.part_lse[(size_t)c * rows + row] - M) : 0.f;   // 0 for an empty chunk
+            float zs = wc;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) zs += __shfl_xor(zs, off);
+            Z += zs;
+            wsh[wave][lane] = wc;
+            __builtin_amdgcn_wave_barrier();
+            const int n = min(64, p.splits - c0);
+#pragma unroll 8
+            for (int j = 0; j < n; ++j) {
+                const float w = wsh[wave][j];
+                const float* src = p.part_o + ((size_t)(c0 + j) * rows + row) * D;
+#pragma unroll
+                for (int r = 0; r < D / 64; ++r) acc[r] = fmaf(w, src[lane + 64 * r], acc[r]);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) p.out[row * D + lane + 64 * r] = to_bf16(Z > 0.f ? acc[r] / Z : 0.f);
+    if (p.lse != nullptr && lane == 0) p.lse[row] = Z > 0.f ? M + logf(Z) : -INFINITY;
+}
+
+template <int D, int NQ>
+hipError_t launch_nq(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s) {
+    DParams p;
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.k = static_cast<const uint16_t*>(a.k);
+    p.v = static_cast<const uint16_t*>(a.v);
+    p.out = static_cast<uint16_t*>(a.out);
+    p.lse = a.lse;
+    p.key_lens = a.key_lens;
+    p.H = a.H;
+    p.Lq = a.Lq;
+    p.Lk = a.Lk;
+    p.causal = a.causal;
+    p.splits = plan.splits;
+    p.chunk = plan.chunk;
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const long long rows = (long long)a.B * a.H * a.Lq;
+    p.part_lse = static_cast<float*>(a.workspace);
+    p.part_o = p.part_lse + (size_t)plan.splits * rows;
+    const long long grid = (long long)a.B * a.H * plan.splits;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_kernel<D, NQ>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.splits == 1) return e;
+    hipLaunchKernelGGL((decode_combine<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, rows);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s) {
+    if (a.Lq <= 1) return launch_nq<D, 1>(a, plan, s);
+    if (a.Lq <= 2) return launch_nq<D, 2>(a, plan, s);
+    if (a.Lq <= 4) return launch_nq<D, 4>(a, plan, s);
+    return launch_nq<D, 8>(a, plan, s);
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int B, int H, int Lq, int Lk, int d, int num_cus) {
+    DecodePlan plan;
+    // step of the kernel: 4 wavefronts x 64/(d/8) rows; chunks of about
+    // 256 KiB of keys and values, and at least 4 workgroups per compute
+    // unit, so that chunks of uneven length (key_lens) still balance; never
+    // chunks under 4 steps
+    const int step = kWaves * (64 / (d / 8));
+    const long long slices = (long long)B * H;
+    const long long target_keys = (256LL << 10) / (4LL * d);
+    long long splits = (Lk + target_keys - 1) / target_keys;
+    const long long want = 4LL * num_cus;
+    if (slices * splits < want) splits = (want + slices - 1) / slices;
+    const long long max_splits = (Lk + 4LL * step - 1) / (4LL * step);
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    long long chunk = (Lk + splits - 1) / splits;
+    chunk = (chunk + step - 1) / step * step;
+    splits = (Lk + chunk - 1) / chunk;
+    plan.splits = (int)splits;
+    plan.chunk = (int)chunk;
+    const long long rows = (long long)B * H * Lq;
+    plan.workspace_bytes = splits > 1 ? (size_t)splits * rows * (size_t)(d + 1) * sizeof(float) : 0;
+    return plan;
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s) {
+    if (a.Lq < 1 || a.Lq > kDecodeMaxLq) return hipErrorInvalidValue;
+    if (a.d == 128) return launch_d<128>(a, plan, s);
+    if (a.d == 64) return launch_d<64>(a, plan, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

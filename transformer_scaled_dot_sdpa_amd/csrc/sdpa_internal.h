@@ -39,6 +39,31 @@ struct BwdArgs {
     int causal;
 };
 
+// Arguments of the decode-shaped forward: FwdArgs plus the caller's
+// workspace (partial results of the key chunks).
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;               // may be null
+    const int32_t* key_lens;  // may be null
+    void* workspace;          // plan.workspace_bytes, 4-byte aligned (unused with one chunk)
+    int B, H, Lq, Lk, d;
+    int causal;
+};
+
+// Largest number of query rows the decode kernel takes.
+constexpr int kDecodeMaxLq = 8;
+
+// How a decode call is split over keys.
+struct DecodePlan {
+    int splits;               // key chunks per (b, h)
+    int chunk;                // keys per chunk
+    size_t workspace_bytes;   // 0 when splits == 1
+};
+DecodePlan plan_decode(int B, int H, int Lq, int Lk, int d, int num_cus);
+
 // One bf16 tile configuration.  br = rows of Q per workgroup
 // (32 per wavefront), bc = keys per K/V tile.
 struct Bf16Tile {
@@ -62,6 +87,7 @@ hipError_t launch_fwd_bf16_pp(const FwdArgs& a, const Bf16Tile& t, hipStream_t s
 hipError_t launch_fwd_bf16_wide(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
 
 }  // namespace sdpa

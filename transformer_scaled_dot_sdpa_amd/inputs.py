@@ -74,6 +74,20 @@ WORKLOADS = {
                                   causal=True, scale=0.5, seed=4,
                                   note="large-model causal self-attention"),
 }
+# Decode-shaped workloads (one new query per step against the cached keys of
+# every earlier position; cookipedia article, "全体").  Shapes: GPT-3's heads
+# and its 2048-token context (formula page, "起源" and "応用"); the base
+# model's 8 heads of 64 for a single long sequence.  Batch sizes and the
+# length range are not on the pages.
+DECODE_WORKLOADS = {
+    "decode_d128": Workload("decode_d128", 16, 96, 1, 2048, 128, "bf16",
+                            key_lens=(1024, 2048), seed=5,
+                            note="decode step, 96 heads of 128, context 1024..2048"),
+    "decode_d64_single": Workload("decode_d64_single", 1, 8, 1, 4096, 64, "bf16", seed=6,
+                                  note="decode step, one sequence, 8 heads of 64, context 4096"),
+}
+WORKLOADS.update(DECODE_WORKLOADS)
+
 WORKLOAD_ORDER = ["toy_f32", "encoder_d64", "decoder_causal_d64",
                   "cross_padded_d64", "large_causal_d128"]
 
