@@ -106,6 +106,9 @@ class Oracle:
         lib.oracle_sdpa_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64,
                                         i32, vp, dbl, vp, vp, vp, i32]
         lib.oracle_sdpa_bwd.restype = i32
+        lib.oracle_sdpa_ex.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64,
+                                       i32, vp, dbl, vp, vp, vp, i32]
+        lib.oracle_sdpa_ex.restype = i32
         self._lib = lib
         self.path = lib_path
 
@@ -189,6 +192,40 @@ class Oracle:
         return dq, dk, dv
 
 
+    def sdpa_ex(self, q, k, v, causal: bool = False, key_lens=None, tau: float | None = None,
+                mask=None, bf16: bool = False, nthreads: int = 0):
+        """General form: v of its own width d_v, divisor ``tau`` (default
+        sqrt(d_k)), optional additive ``mask`` broadcastable to [B, H, Lq, Lk]
+        (any float dtype; -inf drops a key).  Returns ``(out[B, H, Lq, d_v],
+        lse[B, H, Lq])`` in fp64."""
+        q, dt = _as_input(q, bf16)
+        k, dtk = _as_input(k, bf16)
+        v, dtv = _as_input(v, bf16)
+        if not (dt == dtk == dtv):
+            raise TypeError("q, k, v must share one dtype")
+        if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+            raise ValueError("q, k, v must be [B, H, L, width]")
+        B, H, Lq, d = q.shape
+        Lk, dv = k.shape[2], v.shape[3]
+        if k.shape != (B, H, Lk, d) or v.shape[:3] != (B, H, Lk):
+            raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+        _kl, kl_ptr = _key_lens_arg(key_lens, B)
+        m_ptr = None
+        if mask is not None:
+            mask = np.ascontiguousarray(np.broadcast_to(np.asarray(mask, dtype=np.float64),
+                                                        (B, H, Lq, Lk)))
+            m_ptr = mask.ctypes.data
+        out = np.empty((B, H, Lq, dv), dtype=np.float64)
+        lse = np.empty((B, H, Lq), dtype=np.float64)
+        rc = self._lib.oracle_sdpa_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, dt,
+                                      B, H, Lq, Lk, d, dv, int(bool(causal)), kl_ptr,
+                                      float(tau) if tau is not None else 0.0, m_ptr,
+                                      out.ctypes.data, lse.ctypes.data, int(nthreads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_sdpa_ex failed with code {rc}")
+        return out, lse
+
+
 _lock = threading.Lock()
 _default: Oracle | None = None
 
@@ -210,6 +247,11 @@ def sdpa(q, k, v, **kw):
 def sdpa_rows(q, k, v, rows, **kw):
     """:meth:`Oracle.sdpa_rows` of the default oracle."""
     return default().sdpa_rows(q, k, v, rows, **kw)
+
+
+def sdpa_ex(q, k, v, **kw):
+    """:meth:`Oracle.sdpa_ex` of the default oracle."""
+    return default().sdpa_ex(q, k, v, **kw)
 
 
 def sdpa_bwd(q, k, v, dout, **kw):

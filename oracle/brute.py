@@ -35,6 +35,18 @@ def attention_row(q, keys, values, tau=None):
     return o, math.log(Z)
 
 
+def attention_row_biased(q, keys, values, tau, bias):
+    """One query with an additive term per key on the scaled scores:
+    s_j = q . k_j / tau + bias_j, a_j = e^{s_j} / sum_i e^{s_i} (no max
+    shift), o = sum_j a_j v_j with values of any width.  Returns (o, lse)."""
+    s = [math.fsum(qt * kt for qt, kt in zip(q, k)) / tau + b for k, b in zip(keys, bias)]
+    e = [math.exp(x) for x in s]
+    Z = math.fsum(e)
+    width = len(values[0])
+    o = [math.fsum(e[j] / Z * values[j][t] for j in range(len(values))) for t in range(width)]
+    return o, math.log(Z)
+
+
 def attention(q, k, v, causal=False, key_lens=None, tau=None):
     """Nested lists / arrays q[B][H][Lq][d], k and v [B][H][Lk][d].
 

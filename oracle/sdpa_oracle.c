@@ -42,6 +42,15 @@
  * Inputs may be fp64, fp32 or bf16 (raw 16-bit patterns); every element is
  * widened to fp64 exactly before any arithmetic.  Outputs are fp64.
  *
+ * General form (oracle_sdpa_ex): values of their own width d_v (German
+ * translation, section 3.2.1: queries and keys of dimension d_k, values of
+ * dimension d_v), any divisor tau (the temperature form of section 証明),
+ * and an optional additive mask added to the scaled scores before the
+ * softmax, -inf entries dropping their key as the causal mask does (formula
+ * page, section 応用; the toy model of the cookipedia article, section
+ * "トイモデル", builds its decoder mask this way).  A row whose valid keys all
+ * carry -inf returns o = 0 and lse = -inf, as a row with no valid key.
+ *
  * Backward (oracle_sdpa_bwd): the gradients of a scalar loss L with
  * dL/dO = dout, following the same proof section:
  *   dL/da_j = dout . v_j                    (from the output display)
@@ -286,6 +295,75 @@ int oracle_sdpa_bwd(const void* q, const void* k, const void* v, const void* dou
         }
         free(a);
         free(da);
+    }
+    return bad ? 2 : 0;
+}
+
+/*
+ * General form.  q is [B, H, Lq, d], k is [B, H, Lk, d], v is [B, H, Lk, dv],
+ * out is [B, H, Lq, dv], lse [B, H, Lq], mask NULL or fp64 [B, H, Lq, Lk], all
+ * contiguous row-major.  Per row:
+ *   1. s_j = (q . k_j) / tau + mask_ij   over the valid keys j
+ *   2. m = max_j s_j; if m = -inf the row is empty (o = 0, lse = -inf);
+ *      a_j = e^{s_j - m} / Z with Z = sum_j e^{s_j - m}
+ *   3. o = sum_j a_j v_j (width dv)
+ *   4. lse = m + ln Z
+ */
+int oracle_sdpa_ex(const void* q, const void* k, const void* v, int dtype,
+                   int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d, int64_t dv,
+                   int causal, const int32_t* key_lens, double tau, const double* mask,
+                   double* out, double* lse, int nthreads)
+{
+    if (check_args(q, k, v, dtype, B, H, Lq, Lk, d, causal, out, lse)) return 1;
+    if (dv < 1) return 1;
+    if (!(tau > 0.0)) tau = sqrt((double)d);
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    const int64_t nrows = B * H * Lq;
+    int bad = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* sc = (double*)malloc(sizeof(double) * (size_t)Lk);
+        if (!sc) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t row = 0; row < nrows; ++row) {
+            if (!sc) continue;
+            const int64_t i = row % Lq, bh = row / Lq, b = bh / H;
+            const int64_t n = valid_keys(i, b, Lk, causal, key_lens);
+            double* o = out + row * dv;
+            /* 1. scores plus the additive mask */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < n; ++j) {
+                double z = 0.0;
+                for (int64_t t = 0; t < d; ++t)
+                    z += load_elem(q, dtype, row * d + t) * load_elem(k, dtype, (bh * Lk + j) * d + t);
+                sc[j] = z / tau + (mask ? mask[row * Lk + j] : 0.0);
+                if (sc[j] > m) m = sc[j];
+            }
+            if (n <= 0 || m == -INFINITY) {
+                for (int64_t t = 0; t < dv; ++t) o[t] = 0.0;
+                lse[row] = -INFINITY;
+                continue;
+            }
+            /* 2. weights */
+            double Z = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                sc[j] = exp(sc[j] - m);
+                Z += sc[j];
+            }
+            /* 3. output of width dv */
+            for (int64_t t = 0; t < dv; ++t) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < n; ++j)
+                    acc += sc[j] / Z * load_elem(v, dtype, (bh * Lk + j) * dv + t);
+                o[t] = acc;
+            }
+            /* 4. log-sum-exp */
+            lse[row] = m + log(Z);
+        }
+        free(sc);
     }
     return bad ? 2 : 0;
 }

@@ -467,6 +467,121 @@ def pin_bwd_invariants(orc, seed=23):
                 assert np.all(dq[b, hh, unseen] == 0)
 
 
+# --------------------------------------------------------------------------
+# General form: values of width d_v, any divisor, additive mask
+# --------------------------------------------------------------------------
+
+def pin_ex_worked_example(orc):
+    """The d_k = 4 example through the general form with values of other
+    widths: V = the 8 x 8 identity (d_v = 8) returns the weights themselves
+    (0.634 / 0.141 / 0.067 / 0.032 at divisor 2; fish 0.932 at 1 and 0.217 at
+    8); V = the first two columns of K (d_v = 2) returns the first two printed
+    outputs 0.70, 1.44."""
+    g = _golden("worked_example.json")
+    keys = np.array(g["keys"], dtype=np.float64).reshape(1, 1, 8, 4)
+    q = np.array(g["query"], dtype=np.float64).reshape(1, 1, 1, 4)
+    pr = g["printed"]
+    eye = np.eye(8).reshape(1, 1, 8, 8)
+    w, _ = orc.sdpa_ex(q, keys, eye, tau=pr["divisor"])
+    pw = pr["weights"]
+    for tok, a in zip(g["tokens"], w[0, 0, 0]):
+        assert _printed_close(a, pw.get(tok, pw["others"]), pw["decimals"]), (tok, a)
+    fish = g["tokens"].index("魚")
+    w1, _ = orc.sdpa_ex(q, keys, eye, tau=1.0)
+    w8, _ = orc.sdpa_ex(q, keys, eye, tau=8.0)
+    assert _printed_close(w1[0, 0, 0, fish], pr["fish_weight_divided_by_1"]["value"], 3)
+    assert _printed_close(w8[0, 0, 0, fish], pr["fish_weight_divided_by_8"]["value"], 3)
+    out2, lse = orc.sdpa_ex(q, keys, np.ascontiguousarray(keys[..., :2]))
+    for got, want in zip(out2[0, 0, 0], pr["output"]["value"][:2]):
+        assert _printed_close(got, want, pr["output"]["decimals"]), out2
+    assert _printed_close(math.exp(lse[0, 0, 0]), pr["exp_sum"]["value"], pr["exp_sum"]["decimals"])
+
+
+def pin_ex_additive_causal(orc, seed=24):
+    """A -inf mask on the strict upper triangle (the toy model's additive
+    decoder mask) is the causal mask: same outputs and lse."""
+    rng = np.random.default_rng(seed)
+    for Lq, Lk in ((6, 6), (7, 4), (3, 9)):
+        q = rng.standard_normal((2, 2, Lq, 5))
+        k = rng.standard_normal((2, 2, Lk, 5))
+        v = rng.standard_normal((2, 2, Lk, 3))
+        mask = np.where(np.arange(Lk)[None, :] > np.arange(Lq)[:, None], -np.inf, 0.0)
+        o1, l1 = orc.sdpa_ex(q, k, v, mask=mask)
+        o2, l2 = orc.sdpa_ex(q, k, v, causal=True)
+        assert np.max(np.abs(o1 - o2)) < 1e-14 and np.array_equal(np.isneginf(l1), np.isneginf(l2))
+        fin = np.isfinite(l2)
+        assert np.max(np.abs(l1[fin] - l2[fin])) < 1e-14
+
+
+def pin_ex_mask_shift_and_weights(orc, seed=25):
+    """A mask constant along a row leaves the output and shifts lse by that
+    constant (the ratio identity); with q = 0 every score is 0 and a mask
+    ln w_j makes the weights w_j / sum w, so o = sum w_j v_j / sum w and
+    lse = ln sum w (closed form, no attention code)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, 3, 4, 6))
+    k = rng.standard_normal((1, 3, 5, 6))
+    v = rng.standard_normal((1, 3, 5, 2))
+    c = rng.standard_normal((1, 3, 4, 1)) * 5
+    o0, l0 = orc.sdpa_ex(q, k, v)
+    o1, l1 = orc.sdpa_ex(q, k, v, mask=np.broadcast_to(c, (1, 3, 4, 5)))
+    assert np.max(np.abs(o1 - o0)) < 1e-12
+    assert np.max(np.abs(l1 - (l0 + c[..., 0]))) < 1e-12
+    w = rng.uniform(0.1, 3.0, size=5)
+    o, l = orc.sdpa_ex(np.zeros((1, 1, 1, 6)), k[:, :1], v[:, :1], mask=np.log(w))
+    want = (w[:, None] * v[0, 0]).sum(0) / w.sum()
+    assert np.max(np.abs(o[0, 0, 0] - want)) < 1e-12
+    assert abs(l[0, 0, 0] - math.log(w.sum())) < 1e-12
+
+
+def pin_ex_masked_rows_and_padding(orc, seed=26):
+    """-inf on keys >= len is the key-length mask; a row whose keys all carry
+    -inf is empty: o = 0 and lse = -inf."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((2, 1, 4, 3))
+    k = rng.standard_normal((2, 1, 7, 3))
+    v = rng.standard_normal((2, 1, 7, 5))
+    lens = [5, 2]
+    mask = np.zeros((2, 1, 4, 7))
+    for b, n in enumerate(lens):
+        mask[b, :, :, n:] = -np.inf
+    o1, l1 = orc.sdpa_ex(q, k, v, mask=mask)
+    o2, l2 = orc.sdpa_ex(q, k, v, key_lens=lens)
+    assert np.max(np.abs(o1 - o2)) < 1e-14 and np.max(np.abs(l1 - l2)) < 1e-14
+    mask[1, 0, 2, :] = -np.inf
+    o3, l3 = orc.sdpa_ex(q, k, v, mask=mask)
+    assert np.all(o3[1, 0, 2] == 0) and np.isneginf(l3[1, 0, 2])
+    assert np.all(np.isfinite(o3)) and np.sum(np.isneginf(l3)) == 1
+
+
+def pin_ex_brute_force(orc, seed=27):
+    """General form against the pure-Python route with a bias term, to 1e-12:
+    d_v != d_k, divisors other than sqrt(d_k), finite random masks, causal and
+    key lengths."""
+    from oracle import brute
+    rng = np.random.default_rng(seed)
+    for (B, H, Lq, Lk, d, dv, tau, causal, kl) in ((1, 2, 4, 6, 3, 5, 0.7, False, None),
+                                                   (2, 1, 5, 5, 4, 2, 3.0, True, [3, 5]),
+                                                   (1, 1, 3, 8, 2, 7, None, False, [6])):
+        q = rng.standard_normal((B, H, Lq, d))
+        k = rng.standard_normal((B, H, Lk, d))
+        v = rng.standard_normal((B, H, Lk, dv))
+        mask = rng.standard_normal((B, H, Lq, Lk))
+        o, l = orc.sdpa_ex(q, k, v, causal=causal, key_lens=kl, tau=tau, mask=mask)
+        t = tau if tau is not None else math.sqrt(d)
+        for b in range(B):
+            for h in range(H):
+                for i in range(Lq):
+                    n = Lk if kl is None else min(Lk, kl[b])
+                    if causal:
+                        n = min(n, i + 1)
+                    ro, rl = brute.attention_row_biased(q[b, h, i].tolist(), k[b, h, :n].tolist(),
+                                                        v[b, h, :n].tolist(), t,
+                                                        mask[b, h, i, :n].tolist())
+                    assert np.max(np.abs(o[b, h, i] - np.array(ro))) < 1e-12
+                    assert abs(l[b, h, i] - rl) < 1e-12
+
+
 ALL_PINS = [
     pin_worked_example_output, pin_worked_example_weights, pin_worked_example_scores,
     pin_temperature, pin_two_keys_d64, pin_softmax_row_properties,
@@ -475,4 +590,6 @@ ALL_PINS = [
     pin_brute_force, pin_rows_match_full, pin_input_widening,
     pin_bwd_two_keys_gradient, pin_bwd_finite_differences, pin_bwd_brute_force,
     pin_bwd_invariants,
+    pin_ex_worked_example, pin_ex_additive_causal, pin_ex_mask_shift_and_weights,
+    pin_ex_masked_rows_and_padding, pin_ex_brute_force,
 ]

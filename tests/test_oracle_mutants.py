@@ -45,6 +45,16 @@ MUTANTS = [
      "dv[kv_off + j * d + t] += da[j] * load_elem(dout, dtype, q_off + t);"),
     ("bwd_da_from_k", "z += load_elem(dout, dtype, q_off + t) * load_elem(v, dtype, kv_off + j * d + t);",
      "z += load_elem(dout, dtype, q_off + t) * load_elem(k, dtype, kv_off + j * d + t);"),
+    # general form
+    ("ex_mask_ignored", "sc[j] = z / tau + (mask ? mask[row * Lk + j] : 0.0);", "sc[j] = z / tau;"),
+    ("ex_mask_sign", "sc[j] = z / tau + (mask ? mask[row * Lk + j] : 0.0);",
+     "sc[j] = z / tau - (mask ? mask[row * Lk + j] : 0.0);"),
+    ("ex_mask_transposed", "sc[j] = z / tau + (mask ? mask[row * Lk + j] : 0.0);",
+     "sc[j] = z / tau + (mask ? mask[(bh * Lk + j) * Lq + i] : 0.0);"),
+    ("ex_tau_ignored", "sc[j] = z / tau + (mask", "sc[j] = z / sqrt((double)d) + (mask"),
+    ("ex_value_width_d", "acc += sc[j] / Z * load_elem(v, dtype, (bh * Lk + j) * dv + t);",
+     "acc += sc[j] / Z * load_elem(v, dtype, (bh * Lk + j) * d + t);"),
+    ("ex_all_masked_not_empty", "if (n <= 0 || m == -INFINITY) {", "if (n <= 0) {"),
 ]
 
 
