@@ -28,6 +28,10 @@ in HBM.  W untimed steps, then K timed steps bracketed by
   decode-shaped workload (default ``decode_d128``), timed with HIP events,
   reported as HBM GB/s of algorithmic bytes (the workload is bandwidth
   bound), with ``sdpa_forward`` timed on the same inputs beside it;
+* ``forward_ex``: ``sdpa_forward_ex`` on the main workload's own inputs in
+  the head-interleaved [B, L, H*d] layout, and with an additive fp32 bias
+  (a [Lq, Lk] matrix shared by every slice) on top of the causal mask, each
+  timed with HIP events and reported in TFLOP/s by the headline formula;
 * ``vendor_gemm``: context for the MFMA roofline -- the rate torch.matmul
   (the vendor BLAS) reaches on a large square bf16 product on the same GPU in
   the same run, i.e. what dense matrix cores deliver in practice at the clock
@@ -220,6 +224,49 @@ def backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args, fwd_flops_alg)
                          "kernels": "bwd_delta_kernel, bwd_dq_kernel, bwd_dkdv_kernel"}}
 
 
+def forward_ex_leg(torch, sdpa, w, sets, tkl, stream, args):
+    """sdpa_forward_ex on the first input set: head-interleaved layout, then
+    an additive bias on the scaled scores (plus the workload's own masks)."""
+    import numpy as np
+    tq, tk, tv = sets[0][:3]
+    lse = torch.empty_like(sets[0][4])   # the main leg's outputs stay untouched
+    il = lambda t: t.transpose(1, 2).contiguous().transpose(1, 2)
+    iq, ik, iv = il(tq), il(tk), il(tv)
+    iout = il(torch.empty_like(tq))
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    bias = torch.randn((w.Lq, w.Lk), device="cuda", generator=gen, dtype=torch.float32) * 0.5
+    out = torch.empty_like(tq)
+
+    def timed(fn):
+        steps = max(1, min(args.steps, 20))
+        for _ in range(min(args.warmup, 3)):
+            fn()
+        torch.cuda.synchronize()
+        st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            st[i].record(stream)
+            fn()
+            en[i].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in zip(st, en)])), steps
+
+    ms_il, steps = timed(lambda: sdpa.forward_ex(iq, ik, iv, causal=w.causal, key_lens=tkl, out=iout,
+                                                 lse=lse, stream=stream))
+    ms_mask, _ = timed(lambda: sdpa.forward_ex(tq, tk, tv, causal=w.causal, key_lens=tkl, mask=bias,
+                                               out=out, lse=lse, stream=stream))
+    tf = lambda ms: w.flops / (ms * 1e-3) / 1e12
+    print(f"[bench] forward_ex: interleaved {ms_il*1e3:.1f} us ({tf(ms_il):.1f} TFLOP/s), "
+          f"with bias {ms_mask*1e3:.1f} us ({tf(ms_mask):.1f} TFLOP/s)", file=sys.stderr, flush=True)
+    del iq, ik, iv, iout, bias, out, lse
+    return {"steps": steps,
+            "interleaved": {"layout": "[B, L, H*d_k] for q, k, v and out", "us_per_call": ms_il * 1e3,
+                            "value": tf(ms_il), "unit": "TFLOP/s"},
+            "additive_bias": {"mask": "fp32 [Lq, Lk] shared by every (b, h), plus the workload's masks",
+                              "us_per_call": ms_mask * 1e3, "value": tf(ms_mask), "unit": "TFLOP/s",
+                              "mask_bytes": w.Lq * w.Lk * 4}}
+
+
 def decode_leg(torch, sdpa, inputs, name, args):
     """Time sdpa_decode and, on the same inputs, sdpa_forward."""
     import numpy as np
@@ -283,6 +330,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--decode-workload", default="decode_d128",
                     help="decode-shaped workload of the decode leg ('none' skips it)")
+    ap.add_argument("--no-forward-ex", action="store_true", help="skip the forward_ex leg")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip the vendor GEMM context measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -399,6 +447,8 @@ def main():
     if not args.no_backward and w.dtype == "bf16":
         result["backward"] = backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args,
                                           flops_alg)
+    if not args.no_forward_ex and w.dtype == "bf16":
+        result["forward_ex"] = forward_ex_leg(torch, sdpa, w, sets, tkl, stream, args)
     if args.decode_workload != "none":
         result["decode"] = decode_leg(torch, sdpa, inputs, args.decode_workload, args)
     if not args.no_vendor_gemm:

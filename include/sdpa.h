@@ -102,6 +102,72 @@ sdpa_status_t sdpa_forward(sdpa_handle_t h,
                            int causal, const int32_t* key_lens, void* stream);
 
 /*
+ * Element strides of a [B, H, L, width] view whose last dimension is
+ * contiguous: element (b, h, l, t) sits at base + b*batch + h*head + l*row + t.
+ * A layout with row == 0 stands for the contiguous [B, H, L, width] tensor.
+ * The head-interleaved [B, L, H*width] layout that multi-head attention
+ * produces and concatenates (cookipedia article, section "Transformer の構造";
+ * German translation, section 3.2.2) is batch = L*H*width, head = width,
+ * row = H*width.
+ */
+typedef struct {
+    int64_t batch;
+    int64_t head;
+    int64_t row;
+} sdpa_layout_t;
+
+/*
+ * The general forward: every argument of sdpa_forward plus
+ *   d_v          width of values and outputs (German translation, section
+ *                3.2.1: queries and keys of dimension d_k, values of
+ *                dimension d_v); <= 0 means d_v = d_k.
+ *   *_layout     strides of q, k (width d_k), v, out (width d_v).
+ *   scale        scores are (q . k) * scale; <= 0 means 1/sqrt(d_k).  The
+ *                temperature form of the formula page's section 証明 is
+ *                scale = 1/tau.
+ *   mask         NULL, or an additive fp32 term added to every scaled score
+ *                before the softmax: element (b, h, i, j) of a [B, H, Lq, Lk]
+ *                view with strides mask_layout (batch or head 0 broadcast;
+ *                all zero: one [Lq, Lk] matrix shared by every (b, h)).
+ *                Entries must be finite or -inf; -inf drops the key, as the
+ *                causal mask does (formula page, section 応用; the toy model
+ *                of the cookipedia article, section "トイモデル", builds its
+ *                decoder mask this way).  A row whose valid keys all carry
+ *                -inf gets out = 0 and lse = -inf.
+ * causal and key_lens apply as in sdpa_forward, on top of the mask.
+ */
+typedef struct {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;                 /* [B, H, Lq] contiguous, or NULL */
+    int B, H, Lq, Lk, d_k, d_v;
+    sdpa_layout_t q_layout, k_layout, v_layout, out_layout;
+    int causal;
+    const int32_t* key_lens;
+    float scale;
+    const float* mask;
+    sdpa_layout_t mask_layout;
+} sdpa_forward_desc_t;
+
+/*
+ * Enqueue the general forward described by *desc on `stream`; returns
+ * without waiting.  Handle dtype as sdpa_forward.  bf16: d_k and d_v in
+ * {64, 128}; every stride a multiple of 8 elements and q, k, v, out 16-byte
+ * aligned; each of k and v spanning under 4 GiB per (b, h) slice (Lk * row
+ * stride * 2 bytes); a mask slice under 2 GiB.  fp32: d_k, d_v <= 256, any
+ * strides.  The mask is read fastest when its pointer is 16-byte aligned and
+ * its strides are multiples of 4.
+ * Errors (before anything is enqueued): INVALID_VALUE for desc == NULL, a
+ * NULL tensor, sizes < 1, causal not 0/1, a row stride below the width, a
+ * negative stride, element counts overflowing int64, or out overlapping
+ * any input (by extent); NOT_SUPPORTED for the dtype limits above;
+ * HIP_ERROR if the launch fails.
+ */
+sdpa_status_t sdpa_forward_ex(sdpa_handle_t h, const sdpa_forward_desc_t* desc, void* stream);
+
+/*
  * Enqueue the gradients of one attention forward on `stream`; returns
  * without waiting.
  *

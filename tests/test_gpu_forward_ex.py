@@ -1,0 +1,221 @@
+"""General forward (sdpa_forward_ex) vs the oracle's general form through the
+C ABI: head-interleaved and packed layouts, d_v != d_k, explicit scales,
+additive masks (shared, per batch, with rows masked entirely), alone and
+combined with the causal and key-length masks.
+
+Tolerances as the forward: max-abs 1e-5 (fp32) / 2e-2 (bf16) on outputs of
+order 1, 1e-3 on lse, -inf rows exact.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import announce, assert_close, require_gpu, to_device
+from transformer_scaled_dot_sdpa_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def draw(B, H, L, width, dtype, seed):
+    """[B, H, L, width] values by the generator's recipe (its q slot)."""
+    x, _, _, _ = inputs.generate(B, H, L, 1, width, dtype, seed)
+    return x
+
+
+def interleaved(t):
+    """Device copy of a [B, H, L, w] tensor stored as [B, L, H, w] (the
+    head-interleaved [B, L, H*w] layout), returned as a [B, H, L, w] view."""
+    store = t.transpose(1, 2).contiguous()
+    return store.transpose(1, 2)
+
+
+def run_ex(q, k, v, dtype, layout="contiguous", **kw):
+    import torch
+    import transformer_scaled_dot_sdpa_amd as sdpa
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    if layout == "interleaved":
+        qd, kd, vd = interleaved(qd), interleaved(kd), interleaved(vd)
+        B, H, Lq, _ = q.shape
+        out = interleaved(torch.empty((B, H, Lq, v.shape[3]), dtype=qd.dtype, device="cuda"))
+        kw["out"] = out
+    kl = kw.pop("key_lens", None)
+    if kl is not None:
+        kw["key_lens"] = torch.from_numpy(np.asarray(kl, dtype=np.int32)).cuda()
+    mask = kw.pop("mask", None)
+    if mask is not None:
+        kw["mask"] = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.float32)).cuda()
+    o, l = sdpa.forward_ex(qd, kd, vd, **kw)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), l.cpu().numpy()
+
+
+def oracle_ex(q, k, v, dtype, causal=False, key_lens=None, scale=None, mask=None):
+    import oracle
+    m = None if mask is None else np.asarray(mask, dtype=np.float32).astype(np.float64)
+    return oracle.sdpa_ex(q, k, v, causal=causal, key_lens=key_lens,
+                          tau=(1.0 / scale) if scale else None, mask=m, bf16=(dtype == "bf16"))
+
+
+BF16_CASES = [
+    # B, H, Lq, Lk, d_k, d_v, layout, causal, key_lens, scale
+    (2, 3, 130, 130, 128, 128, "interleaved", True, None, None),
+    (2, 3, 130, 200, 64, 64, "interleaved", False, [77, 200], None),
+    (1, 2, 300, 300, 64, 128, "contiguous", True, None, None),
+    (1, 2, 257, 129, 128, 64, "interleaved", False, None, None),
+    (2, 2, 200, 200, 128, 128, "contiguous", False, [0, 150], 0.05),
+    (1, 3, 96, 160, 64, 128, "interleaved", True, [100], 0.3),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: "q{}k{}dk{}dv{}{}c{}L{}s{}".format(*c[2:]))
+def test_ex_bf16_layouts_widths_scales(case):
+    B, H, Lq, Lk, dk, dv, layout, causal, kl, scale = case
+    seed = 3000 + Lq + Lk + dk + dv
+    announce(f"forward_ex bf16 {case} seed={seed}")
+    q = draw(B, H, Lq, dk, "bf16", seed)
+    k = draw(B, H, Lk, dk, "bf16", seed + 1)
+    v = draw(B, H, Lk, dv, "bf16", seed + 2)
+    o, l = run_ex(q, k, v, "bf16", layout, causal=causal, key_lens=kl, scale=scale)
+    ro, rl = oracle_ex(q, k, v, "bf16", causal, kl, scale)
+    assert_close(o, l, ro, rl, "bf16", f"forward_ex {case}")
+
+
+F32_CASES = [
+    (1, 2, 8, 8, 3, 5, "interleaved", False, None, None),
+    (2, 2, 70, 90, 17, 256, "interleaved", True, [90, 33], 0.7),
+    (1, 3, 40, 40, 64, 1, "contiguous", True, None, None),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "q{}k{}dk{}dv{}{}c{}L{}s{}".format(*c[2:]))
+def test_ex_fp32(case):
+    B, H, Lq, Lk, dk, dv, layout, causal, kl, scale = case
+    seed = 3100 + Lq + Lk + dk + dv
+    announce(f"forward_ex fp32 {case} seed={seed}")
+    q = draw(B, H, Lq, dk, "fp32", seed)
+    k = draw(B, H, Lk, dk, "fp32", seed + 1)
+    v = draw(B, H, Lk, dv, "fp32", seed + 2)
+    o, l = run_ex(q, k, v, "fp32", layout, causal=causal, key_lens=kl, scale=scale)
+    ro, rl = oracle_ex(q, k, v, "fp32", causal, kl, scale)
+    assert_close(o, l, ro, rl, "fp32", f"forward_ex fp32 {case}")
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 64), ("bf16", 128), ("fp32", 8)])
+def test_ex_masks(dtype, dk):
+    """Shared additive causal mask (the toy model's form) equals the causal
+    flag; random finite per-batch masks broadcast over heads; rows masked
+    entirely give out = 0, lse = -inf; mask plus causal plus key lengths."""
+    B, H, Lq, Lk = 2, 3, 150, 150
+    seed = 3200 + dk
+    q = draw(B, H, Lq, dk, dtype, seed)
+    k = draw(B, H, Lk, dk, dtype, seed + 1)
+    v = draw(B, H, Lk, dk, dtype, seed + 2)
+    tri = np.where(np.arange(Lk)[None, :] > np.arange(Lq)[:, None], -np.inf, 0.0).astype(np.float32)
+    announce(f"forward_ex masks {dtype} d{dk}: additive causal")
+    o1, l1 = run_ex(q, k, v, dtype, mask=tri)
+    o2, l2 = run_ex(q, k, v, dtype, causal=True)
+    ro, rl = oracle_ex(q, k, v, dtype, causal=True)
+    assert_close(o1, l1, ro, rl, dtype, "additive causal mask")
+    assert_close(o2, l2, ro, rl, dtype, "causal flag")
+    rng = np.random.default_rng(seed)
+    m = rng.standard_normal((B, 1, Lq, Lk)).astype(np.float32) * 2
+    m[1, 0, 5, :] = -np.inf                 # one row of batch 1 masked entirely
+    m[0, 0, :, 100:] = -np.inf              # a tail masked for every row of batch 0
+    announce(f"forward_ex masks {dtype} d{dk}: random per-batch mask")
+    o, l = run_ex(q, k, v, dtype, mask=m)
+    ro, rl = oracle_ex(q, k, v, dtype, mask=m)
+    assert_close(o, l, ro, rl, dtype, "random mask")
+    assert np.all(o[1, :, 5] == 0) and np.all(np.isneginf(l[1, :, 5]))
+    announce(f"forward_ex masks {dtype} d{dk}: mask + causal + key_lens + interleaved")
+    o, l = run_ex(q, k, v, dtype, layout="interleaved", mask=m, causal=True, key_lens=[120, 7],
+                  scale=0.2)
+    ro, rl = oracle_ex(q, k, v, dtype, causal=True, key_lens=[120, 7], scale=0.2, mask=m)
+    assert_close(o, l, ro, rl, dtype, "mask + causal + key_lens")
+
+
+def test_ex_packed_qkv_and_contiguous_identity():
+    """q, k, v read out of one packed [B, L, 3, H, d] buffer; and on
+    contiguous tensors with default arguments forward_ex is the forward,
+    bit for bit."""
+    import torch
+    import transformer_scaled_dot_sdpa_amd as sdpa
+    B, H, L, d = 2, 4, 200, 128
+    q = draw(B, H, L, d, "bf16", 3300)
+    k = draw(B, H, L, d, "bf16", 3301)
+    v = draw(B, H, L, d, "bf16", 3302)
+    packed = torch.empty((B, L, 3, H, d), dtype=torch.bfloat16, device="cuda")
+    for idx, x in enumerate((q, k, v)):
+        packed[:, :, idx] = to_device(x, "bf16").transpose(1, 2)
+    views = [packed[:, :, idx].transpose(1, 2) for idx in range(3)]
+    announce("forward_ex packed qkv")
+    o, l = sdpa.forward_ex(*views, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_ex(q, k, v, "bf16", causal=True)
+    assert_close(o.float().cpu().numpy(), l.cpu().numpy(), ro, rl, "bf16", "packed qkv")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    o1, l1 = sdpa.forward(qd, kd, vd, causal=True)
+    o2, l2 = sdpa.forward_ex(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_ex_large_interleaved_sampled_rows():
+    """The large causal workload in the head-interleaved layout at full size;
+    sampled rows against the oracle."""
+    import torch
+    import oracle
+    import transformer_scaled_dot_sdpa_amd as sdpa
+    w = inputs.WORKLOADS["large_causal_d128"]
+    announce("forward_ex large_causal_d128 interleaved: generating")
+    q, k, v, _ = inputs.generate_workload(w)
+    qd, kd, vd = (interleaved(to_device(x, "bf16")) for x in (q, k, v))
+    announce("forward_ex large_causal_d128 interleaved: running")
+    o, l = sdpa.forward_ex(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4321)
+    rows = []
+    for b in range(w.B):
+        for hh in (0, int(rng.integers(1, w.H - 1)), w.H - 1):
+            base = (b * w.H + hh) * w.Lq
+            rows += [base + i for i in (0, 1, 63, 64, 127, 128, 2047, 4095)]
+            rows += [base + int(i) for i in rng.integers(0, w.Lq, size=4)]
+    rows = np.array(sorted(set(rows)), dtype=np.int64)
+    ro, rl = oracle.sdpa_rows(q, k, v, rows, causal=True, bf16=True)
+    og = o.float().cpu().numpy().reshape(-1, w.d)[rows]
+    lg = l.cpu().numpy().reshape(-1)[rows]
+    assert_close(og, lg, ro, rl, "bf16", "large interleaved sampled rows")
+
+
+def test_ex_validation():
+    import torch
+    from transformer_scaled_dot_sdpa_amd import binding as b
+    h = b.handle_for(b.DTYPE_BF16, 0)
+    x = torch.zeros(2, 2, 64, 128, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros_like(x)
+    o = torch.zeros_like(x)
+
+    def desc(**kw):
+        d = b.ForwardDesc()
+        d.q, d.k, d.v, d.out = x.data_ptr(), y.data_ptr(), y.data_ptr(), o.data_ptr()
+        d.B, d.H, d.Lq, d.Lk, d.d_k, d.d_v = 2, 2, 64, 64, 128, 128
+        for key, val in kw.items():
+            setattr(d, key, val)
+        return d
+
+    assert b.sdpa_forward_ex(h, desc(), None) == b.SUCCESS
+    torch.cuda.synchronize()
+    assert b.load_library().sdpa_forward_ex(h, None, None) == b.INVALID_VALUE
+    assert b.sdpa_forward_ex(h, desc(q=None), None) == b.INVALID_VALUE
+    assert b.sdpa_forward_ex(h, desc(out=x.data_ptr()), None) == b.INVALID_VALUE       # out aliases q
+    assert b.sdpa_forward_ex(h, desc(q_layout=b.Layout(0, 0, 64)), None) == b.INVALID_VALUE  # row < d_k
+    assert b.sdpa_forward_ex(h, desc(q_layout=b.Layout(-8, 0, 128)), None) == b.INVALID_VALUE
+    assert b.sdpa_forward_ex(h, desc(d_v=96), None) == b.NOT_SUPPORTED
+    assert b.sdpa_forward_ex(h, desc(k_layout=b.Layout(8448, 4224, 132)), None) == b.NOT_SUPPORTED
+    m = torch.zeros(64, 64, device="cuda")
+    assert b.sdpa_forward_ex(h, desc(mask=m.data_ptr()), None) == b.SUCCESS
+    torch.cuda.synchronize()
+    assert b.sdpa_forward_ex(h, desc(mask=m.data_ptr() + 2), None) == b.INVALID_VALUE   # not float aligned

@@ -6,7 +6,9 @@ HIP kernels (see ``include/sdpa.h`` for the C ABI).  The shared library is
 loaded on first use; ``python -m transformer_scaled_dot_sdpa_amd.build``
 builds it.  ``backward(q, k, v, out, lse, dout, ...)`` returns the gradients
 (dq, dk, dv) of that forward, also in HIP kernels; ``decode(q, k, v, ...)``
-is the forward for 1..8 query rows, split over key chunks.
+is the forward for 1..8 query rows, split over key chunks; ``forward_ex``
+takes strided (e.g. head-interleaved) views, d_v != d_k, a scale and an
+additive mask.
 """
 from .binding import (SdpaError, backward, decode, decode_workspace_size, forward,  # noqa: F401
-                      kernel_name, load_library, LIB_PATH, EXPORTED)
+                      forward_ex, kernel_name, load_library, LIB_PATH, EXPORTED)

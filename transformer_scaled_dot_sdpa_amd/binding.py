@@ -21,9 +21,26 @@ SUCCESS, INVALID_VALUE, NOT_SUPPORTED, HIP_ERROR, ALLOC_FAILED = 0, 1, 2, 3, 4
 DTYPE_FP32, DTYPE_BF16 = 0, 1
 
 # Every symbol include/sdpa.h declares.
-EXPORTED = ("sdpa_create", "sdpa_forward", "sdpa_backward", "sdpa_decode",
+EXPORTED = ("sdpa_create", "sdpa_forward", "sdpa_forward_ex", "sdpa_backward", "sdpa_decode",
             "sdpa_decode_workspace_size", "sdpa_destroy", "sdpa_status_string",
             "sdpa_kernel_name")
+
+
+class Layout(ctypes.Structure):
+    """``sdpa_layout_t``: element strides of batch, head and row."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("row", ctypes.c_int64)]
+
+
+class ForwardDesc(ctypes.Structure):
+    """``sdpa_forward_desc_t``."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("B", ctypes.c_int), ("H", ctypes.c_int), ("Lq", ctypes.c_int),
+                ("Lk", ctypes.c_int), ("d_k", ctypes.c_int), ("d_v", ctypes.c_int),
+                ("q_layout", Layout), ("k_layout", Layout), ("v_layout", Layout),
+                ("out_layout", Layout), ("causal", ctypes.c_int),
+                ("key_lens", ctypes.c_void_p), ("scale", ctypes.c_float),
+                ("mask", ctypes.c_void_p), ("mask_layout", Layout)]
 
 
 class SdpaError(RuntimeError):
@@ -55,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.sdpa_forward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                          i32, vp, vp]
             lib.sdpa_forward.restype = i32
+            lib.sdpa_forward_ex.argtypes = [vp, ctypes.POINTER(ForwardDesc), vp]
+            lib.sdpa_forward_ex.restype = i32
             lib.sdpa_backward.argtypes = [vp] * 11 + [i32] * 6 + [vp, vp]
             lib.sdpa_backward.restype = i32
             lib.sdpa_decode.argtypes = [vp] * 6 + [i32] * 6 + [vp, vp, ctypes.c_size_t, vp]
@@ -102,6 +121,11 @@ def sdpa_backward(handle, q, k, v, out, dout, lse, delta, dq, dk, dv, B, H, Lq, 
     return load_library().sdpa_backward(handle, q, k, v, out, dout, lse, delta, dq, dk, dv,
                                         int(B), int(H), int(Lq), int(Lk), int(d_k), int(causal),
                                         key_lens, stream)
+
+
+def sdpa_forward_ex(handle, desc: ForwardDesc, stream) -> int:
+    """Raw ``sdpa_forward_ex``; returns the status code."""
+    return load_library().sdpa_forward_ex(handle, ctypes.byref(desc), stream)
 
 
 def sdpa_decode(handle, q, k, v, out, lse, B, H, Lq, Lk, d_k, causal, key_lens, workspace,
@@ -195,6 +219,81 @@ def forward(q, k, v, causal: bool = False, key_lens=None, out=None, lse=None,
                       B, H, Lq, Lk, d, int(bool(causal)), kl_ptr, stream.cuda_stream)
     if st != SUCCESS:
         raise SdpaError(st, "sdpa_forward")
+    return out, lse
+
+
+def _layout_of(t, name):
+    """Strides of a 4-d [B, H, L, width] tensor view (last dimension contiguous)."""
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be a 4-d [B, H, L, width] view")
+    sb, sh, sl, st = t.stride()
+    if st != 1 and t.shape[3] > 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return Layout(sb, sh, sl)
+
+
+def forward_ex(q, k, v, causal: bool = False, key_lens=None, scale=None, mask=None, out=None,
+               lse=None, need_lse: bool = True, stream=None):
+    """General forward: ``q``, ``k`` ([.., d_k]) and ``v`` ([.., d_v]) are
+    [B, H, L, width] views with any strides whose last dimension is
+    contiguous -- e.g. ``x.view(B, L, H, d).transpose(1, 2)`` for the
+    head-interleaved [B, L, H*d] layout.  ``scale`` multiplies q.k (default
+    1/sqrt(d_k)); ``mask`` is an additive float32 tensor broadcastable to
+    [B, H, Lq, Lk] (last dimension contiguous; -inf drops a key).  ``out``
+    may be a preallocated [B, H, Lq, d_v] view of any strides.  Returns
+    ``(out, lse)``."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q's dtype and device")
+    B, H, Lq, dk = q.shape
+    Lk, dv = k.shape[2], v.shape[3]
+    if k.shape != (B, H, Lk, dk) or v.shape[:3] != (B, H, Lk):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    code = _dtype_code(q)
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    if out is None:
+        out = torch.empty((B, H, Lq, dv), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, H, Lq, dv) or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must be a [B, H, Lq, d_v] view of q's dtype on q's device")
+    if lse is None and need_lse:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, Lq) or lse.dtype != torch.float32
+                            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be float32 [B, H, Lq] on q's device")
+    desc = ForwardDesc()
+    desc.q, desc.k, desc.v, desc.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    desc.lse = lse.data_ptr() if lse is not None else None
+    desc.B, desc.H, desc.Lq, desc.Lk, desc.d_k, desc.d_v = B, H, Lq, Lk, dk, dv
+    desc.q_layout = _layout_of(q, "q")
+    desc.k_layout = _layout_of(k, "k")
+    desc.v_layout = _layout_of(v, "v")
+    desc.out_layout = _layout_of(out, "out")
+    desc.causal = int(bool(causal))
+    desc.key_lens = None
+    if key_lens is not None:
+        if (key_lens.dtype != torch.int32 or key_lens.shape != (B,) or key_lens.device != q.device
+                or not key_lens.is_contiguous()):
+            raise ValueError("key_lens must be a contiguous int32 [B] tensor on q's device")
+        desc.key_lens = key_lens.data_ptr()
+    desc.scale = float(scale) if scale is not None else 0.0
+    desc.mask = None
+    if mask is not None:
+        if mask.dtype != torch.float32 or mask.device != q.device:
+            raise ValueError("mask must be float32 on q's device")
+        mv = mask.expand(B, H, Lq, Lk)
+        ml = _layout_of(mv, "mask")
+        if ml.row == 0:
+            raise ValueError("mask rows must not be broadcast")
+        desc.mask = mv.data_ptr()
+        desc.mask_layout = ml
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = sdpa_forward_ex(handle_for(code, dev), desc, stream.cuda_stream)
+    if st != SUCCESS:
+        raise SdpaError(st, "sdpa_forward_ex")
     return out, lse
 
 

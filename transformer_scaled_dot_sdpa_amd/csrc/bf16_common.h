@@ -38,8 +38,21 @@ struct KParams {
     int num_items;     // work items = (b, h, query block) triples
     int upi;           // work items per scheduling unit (1, or 2: a long/short pair)
     int num_units;     // ceil(num_items / upi)
-    float scale_log2;  // log2(e) / sqrt(d)
+    float scale_log2;  // log2(e) * scale (scale = 1 / sqrt(d) unless given)
+    // Element strides of the [B, H, L, width] views (the main kernel only;
+    // the other kernels take contiguous tensors): batch, head, row.
+    long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+    int q_sl, k_sl, v_sl, o_sl;
+    // Additive fp32 mask on the scaled scores (MASK kernels): [B, H, Lq, Lk]
+    // view with strides m_sb, m_sh (0 broadcasts), m_sl; inv_scale = 1 / scale
+    // turns it into raw-score units.
+    const float* __restrict__ mask;
+    long long m_sb, m_sh;
+    int m_sl;
+    float inv_scale;
+    int mask_vec;      // mask rows and slices 16-byte aligned: vector loads
 };
+
 
 // LDS row of key j inside a K tile: bits 2 and 3 swapped (an involution).
 // With this order the S^T accumulator of lane (n, h) holds, at index r,

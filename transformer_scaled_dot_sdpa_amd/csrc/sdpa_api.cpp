@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <new>
+#include <utility>
 
 #include "sdpa_internal.h"
 
@@ -37,6 +38,37 @@ bool mul_fits(long long a, long long b, long long c, long long d, long long* r) 
 }
 
 bool is_gfx950(const char* arch) { return strncmp(arch, "gfx950", 6) == 0; }
+
+// Resolved strides of one [B, H, L, width] view and its extent in elements
+// (from the base to one past the last element).
+struct View {
+    long long sb, sh, sl;
+    long long extent;
+};
+
+// false: invalid layout (negative stride, row stride under the width, or an
+// extent that overflows int64).
+bool resolve_view(const sdpa_layout_t& lay, long long B, long long H, long long L, long long width,
+                  View* v) {
+    if (lay.row == 0) {
+        v->sl = width;
+        v->sh = L * width;
+        v->sb = H * L * width;
+    } else {
+        if (lay.batch < 0 || lay.head < 0 || lay.row < width) return false;
+        v->sb = lay.batch;
+        v->sh = lay.head;
+        v->sl = lay.row;
+    }
+    // extent = (B-1) sb + (H-1) sh + (L-1) sl + width, without overflow
+    long long e = width;
+    for (auto [n, st] : {std::pair<long long, long long>{B - 1, v->sb}, {H - 1, v->sh}, {L - 1, v->sl}}) {
+        if (st != 0 && n > (INT64_MAX - e) / st) return false;
+        e += n * st;
+    }
+    v->extent = e;
+    return true;
+}
 
 }  // namespace
 
@@ -122,6 +154,7 @@ sdpa_status_t sdpa_forward(sdpa_handle_t h, const void* q, const void* k, const 
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.key_lens = key_lens;
     a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk; a.d = d_k; a.causal = causal;
     a.num_cus = h->num_cus;
+    a.set_contiguous();
 
     sdpa::Bf16Tile tile;
     if (h->dtype == SDPA_DTYPE_BF16) {
@@ -213,6 +246,105 @@ sdpa_status_t sdpa_backward(sdpa_handle_t h, const void* q, const void* k, const
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = h->dtype == SDPA_DTYPE_BF16 ? sdpa::launch_bwd_bf16(a, s) : sdpa::launch_bwd_f32(a, s);
+    if (cur != h->device) (void)hipSetDevice(cur);
+    return e == hipSuccess ? SDPA_STATUS_SUCCESS : SDPA_STATUS_HIP_ERROR;
+}
+
+sdpa_status_t sdpa_forward_ex(sdpa_handle_t h, const sdpa_forward_desc_t* desc, void* stream) {
+    if (h == nullptr || desc == nullptr) return SDPA_STATUS_INVALID_VALUE;
+    const sdpa_forward_desc_t& d = *desc;
+    if (d.q == nullptr || d.k == nullptr || d.v == nullptr || d.out == nullptr)
+        return SDPA_STATUS_INVALID_VALUE;
+    if (d.B < 1 || d.H < 1 || d.Lq < 1 || d.Lk < 1 || d.d_k < 1) return SDPA_STATUS_INVALID_VALUE;
+    if (d.causal != 0 && d.causal != 1) return SDPA_STATUS_INVALID_VALUE;
+    const int dv = d.d_v > 0 ? d.d_v : d.d_k;
+    View vq, vk, vv, vo, vm;
+    if (!resolve_view(d.q_layout, d.B, d.H, d.Lq, d.d_k, &vq) ||
+        !resolve_view(d.k_layout, d.B, d.H, d.Lk, d.d_k, &vk) ||
+        !resolve_view(d.v_layout, d.B, d.H, d.Lk, dv, &vv) ||
+        !resolve_view(d.out_layout, d.B, d.H, d.Lq, dv, &vo))
+        return SDPA_STATUS_INVALID_VALUE;
+    if (d.mask != nullptr) {
+        sdpa_layout_t ml = d.mask_layout;
+        if (ml.row == 0) ml.row = d.Lk;   // all zero: one shared [Lq, Lk] matrix
+        if (!resolve_view(ml, d.B, d.H, d.Lq, d.Lk, &vm)) return SDPA_STATUS_INVALID_VALUE;
+    }
+    const bool bf16 = h->dtype == SDPA_DTYPE_BF16;
+    const size_t esz = bf16 ? 2 : 4;
+    for (const View* v : {&vq, &vk, &vv, &vo})
+        if ((unsigned long long)v->extent > SIZE_MAX / esz) return SDPA_STATUS_INVALID_VALUE;
+    const size_t bl = (size_t)d.B * d.H * d.Lq * sizeof(float);
+    const size_t bo = (size_t)vo.extent * esz;
+    // out (and lse) must not overlap anything read
+    struct Span { const void* p; size_t n; };
+    const Span reads[] = {{d.q, (size_t)vq.extent * esz}, {d.k, (size_t)vk.extent * esz},
+                          {d.v, (size_t)vv.extent * esz},
+                          {d.mask, d.mask ? (size_t)vm.extent * 4 : 0}};
+    for (const Span& r : reads) {
+        if (r.p == nullptr || r.n == 0) continue;
+        if (overlaps(d.out, bo, r.p, r.n)) return SDPA_STATUS_INVALID_VALUE;
+        if (d.lse != nullptr && overlaps(d.lse, bl, r.p, r.n)) return SDPA_STATUS_INVALID_VALUE;
+    }
+    if (d.lse != nullptr && overlaps(d.lse, bl, d.out, bo)) return SDPA_STATUS_INVALID_VALUE;
+    if (d.lse != nullptr && reinterpret_cast<uintptr_t>(d.lse) % alignof(float) != 0)
+        return SDPA_STATUS_INVALID_VALUE;
+    if (d.key_lens != nullptr && reinterpret_cast<uintptr_t>(d.key_lens) % alignof(int32_t) != 0)
+        return SDPA_STATUS_INVALID_VALUE;
+    if (d.mask != nullptr && reinterpret_cast<uintptr_t>(d.mask) % alignof(float) != 0)
+        return SDPA_STATUS_INVALID_VALUE;
+
+    if (bf16) {
+        if ((d.d_k != 64 && d.d_k != 128) || (dv != 64 && dv != 128)) return SDPA_STATUS_NOT_SUPPORTED;
+        for (const void* p : {d.q, d.k, d.v, (const void*)d.out})
+            if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return SDPA_STATUS_NOT_SUPPORTED;
+        for (const View* v : {&vq, &vk, &vv, &vo})
+            if (v->sb % 8 != 0 || v->sh % 8 != 0 || v->sl % 8 != 0) return SDPA_STATUS_NOT_SUPPORTED;
+        // buffer loads address a (b, h) slice of k and v with 32-bit offsets
+        if ((long long)d.Lk * vk.sl * 2 >= (1LL << 32) || (long long)d.Lk * vv.sl * 2 >= (1LL << 32))
+            return SDPA_STATUS_NOT_SUPPORTED;
+        if (vq.sl > INT32_MAX || vo.sl > INT32_MAX) return SDPA_STATUS_NOT_SUPPORTED;
+        if (d.mask != nullptr && ((long long)(d.Lq - 1) * vm.sl + d.Lk) * 4 >= (1LL << 31))
+            return SDPA_STATUS_NOT_SUPPORTED;
+    } else {
+        if (d.d_k > 256 || dv > 256) return SDPA_STATUS_NOT_SUPPORTED;
+        for (const void* p : {d.q, d.k, d.v, (const void*)d.out})
+            if (reinterpret_cast<uintptr_t>(p) % alignof(float) != 0) return SDPA_STATUS_INVALID_VALUE;
+        for (const View* v : {&vq, &vk, &vv, &vo})
+            if (v->sl > INT32_MAX) return SDPA_STATUS_NOT_SUPPORTED;
+        if (d.mask != nullptr && vm.sl > INT32_MAX) return SDPA_STATUS_NOT_SUPPORTED;
+    }
+
+    sdpa::FwdArgs a;
+    a.q = d.q; a.k = d.k; a.v = d.v; a.out = d.out; a.lse = d.lse; a.key_lens = d.key_lens;
+    a.B = d.B; a.H = d.H; a.Lq = d.Lq; a.Lk = d.Lk; a.d = d.d_k; a.dv = dv; a.causal = d.causal;
+    a.num_cus = h->num_cus;
+    a.q_sb = vq.sb; a.q_sh = vq.sh; a.q_sl = (int)vq.sl;
+    a.k_sb = vk.sb; a.k_sh = vk.sh; a.k_sl = (int)vk.sl;
+    a.v_sb = vv.sb; a.v_sh = vv.sh; a.v_sl = (int)vv.sl;
+    a.o_sb = vo.sb; a.o_sh = vo.sh; a.o_sl = (int)vo.sl;
+    a.scale = d.scale > 0.f ? d.scale : 0.f;
+    a.mask = d.mask;
+    a.m_sb = d.mask ? vm.sb : 0; a.m_sh = d.mask ? vm.sh : 0; a.m_sl = d.mask ? (int)vm.sl : 0;
+
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    if (cur != h->device && hipSetDevice(h->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (bf16) {
+        // the main kernel's default tile: the one kernel with strides, d_v,
+        // scale and mask
+        const sdpa::Bf16Tile tile{d.d_k, 64, 4, 0, nullptr};
+        e = sdpa::launch_fwd_bf16(a, tile, s);
+    } else {
+        e = sdpa::launch_fwd_f32(a, s);
+    }
     if (cur != h->device) (void)hipSetDevice(cur);
     return e == hipSuccess ? SDPA_STATUS_SUCCESS : SDPA_STATUS_HIP_ERROR;
 }

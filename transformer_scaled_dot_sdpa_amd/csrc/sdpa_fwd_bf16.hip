@@ -50,24 +50,30 @@ namespace {
 
 using namespace bf16k;
 
-template <int D, int BC, int NW, bool CAUSAL, bool LENS>
+// D: width of queries and keys; DV: width of values and outputs.  MASK adds
+// an fp32 bias to the scaled scores.  Tensor rows are addressed through the
+// strides in KParams (contiguous or head-interleaved layouts alike).
+template <int D, int DV, int BC, int NW, bool CAUSAL, bool LENS, bool MASK>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     constexpr int NT = NW * 64;
     constexpr int BR = NW * 32;
-    constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int KCH = BC * CPR / NT;         // 16-byte loads per thread per tile
-    constexpr int TILE = BC * D;               // elements per K or V tile
+    constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+    constexpr int CPRV = DV / 8;               // 16-byte chunks per value row
+    constexpr int KCH = BC * CPR / NT;         // 16-byte K loads per thread per tile
+    constexpr int KCHV = BC * CPRV / NT;       // 16-byte V loads per thread per tile
+    constexpr int TILE = BC * D;               // elements per K tile
+    constexpr int TILEV = BC * DV;             // elements per V tile
     constexpr int NKT = BC / 32;               // 32-key sub-tiles
-    constexpr int NDT = D / 32;                // 32-wide output column tiles
+    constexpr int NDT = DV / 32;               // 32-wide output column tiles
     constexpr int NKS = D / 16;                // k-steps of the Q.K^T product
-    static_assert((BC * CPR) % NT == 0, "tile must split evenly over threads");
+    static_assert((BC * CPR) % NT == 0 && (BC * CPRV) % NT == 0, "tile must split evenly over threads");
     static_assert(BC % 32 == 0, "BC must be a multiple of 32");
 
     // K and V tiles, double buffered.  Four separate arrays rather than one:
     // the compiler can then tell that the direct-to-LDS loads into one buffer
     // never alias the reads of the other, and does not make those reads wait
     // for the loads in flight (the tile barrier provides the real ordering).
-    __shared__ __align__(16) uint16_t k_lds0[TILE], k_lds1[TILE], v_lds0[TILE], v_lds1[TILE];
+    __shared__ __align__(16) uint16_t k_lds0[TILE], k_lds1[TILE], v_lds0[TILEV], v_lds1[TILEV];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -83,13 +89,18 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     // tile offset in a scalar register and the per-lane offset from a fixed
     // register; the buffer ends at the valid key length, so rows past it
     // arrive as zeros without being read.
-    uint32_t k_boff[KCH], v_boff[KCH];
+    uint32_t k_boff[KCH], v_boff[KCHV];
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
         const int s = (wave * KCH + u) * 64 + lane;
         const int row = s / CPR, pc = s % CPR;
-        k_boff[u] = (k_lds_row(row) * D + ((pc ^ k_swz<D>(row)) << 3)) * 2;
-        v_boff[u] = (row * D + ((pc ^ v_swz<D>(row)) << 3)) * 2;
+        k_boff[u] = (k_lds_row(row) * p.k_sl + ((pc ^ k_swz<D>(row)) << 3)) * 2;
+    }
+#pragma unroll
+    for (int u = 0; u < KCHV; ++u) {
+        const int s = (wave * KCHV + u) * 64 + lane;
+        const int row = s / CPRV, pc = s % CPRV;
+        v_boff[u] = (row * p.v_sl + ((pc ^ v_swz<DV>(row)) << 3)) * 2;
     }
     // ---- per-lane LDS read offsets (elements) inside a tile
     // K operand: row kt*32 + n, chunk (2ks + h) ^ swz  -> one base per ks,
@@ -109,7 +120,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const int col = dt * 32 + colg;
-            v_rd[dt] = row * D + (((col >> 3) ^ v_swz<D>(row)) << 3) + (col & 7);
+            v_rd[dt] = row * DV + (((col >> 3) ^ v_swz<DV>(row)) << 3) + (col & 7);
         }
     }
 
@@ -122,6 +133,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     int bh, qb;
     item_block<CAUSAL>(item, p.num_qb, &bh, &qb);
     const int b = bh / p.H;
+    const int hh = bh - b * p.H;
     const int q0 = qb * BR;
 
     int kv_len = p.Lk;
@@ -137,42 +149,52 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     const int qrow = q0w + n;
     const int wave_kv_end = CAUSAL ? min(kv_len, q0w + 32) : kv_len;
 
-    const size_t q_base = (size_t)bh * p.Lq * D;
-    const uint16_t* kg = p.k + (size_t)bh * p.Lk * D;
-    const uint16_t* vg = p.v + (size_t)bh * p.Lk * D;
+    const uint16_t* qg = p.q + b * p.q_sb + hh * p.q_sh;
+    const uint16_t* kg = p.k + b * p.k_sb + hh * p.k_sh;
+    const uint16_t* vg = p.v + b * p.v_sb + hh * p.v_sh;
 
     // ---- Q^T operand fragments, kept in registers for the whole loop.  Rows
     // past Lq load the last valid row; their results are never stored.
     bf16x8 qf[NKS];
     {
         const int qr = qrow < p.Lq ? qrow : p.Lq - 1;
-        const i16x8* src = reinterpret_cast<const i16x8*>(p.q + q_base + (size_t)qr * D + 8 * h);
+        const i16x8* src = reinterpret_cast<const i16x8*>(qg + (size_t)qr * p.q_sl + 8 * h);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
     }
 
-    const uint32_t kv_bytes = (uint32_t)kv_len * D * 2;
+    // rows at or past kv_len start at or past these byte counts
+    const uint32_t k_bytes = (uint32_t)kv_len * p.k_sl * 2;
+    const uint32_t v_bytes = (uint32_t)kv_len * p.v_sl * 2;
     // Load u of K or V tile t into LDS buffer buf.  t < 0 asks for nothing:
     // the buffer then has zero length and the load only writes zeros into a
     // buffer no wavefront reads any more (so the instruction needs no branch
     // around it and the surrounding MFMA code stays one block).
     auto load_k = [&](int t, int buf, int u) __attribute__((always_inline)) {
-        const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * D * 2;
+        const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * p.k_sl * 2;
         lds_void* kd = (lds_void*)((buf ? k_lds1 : k_lds0) + (wave * KCH + u) * 64 * 8);
-        buffer_load_lds16(kg, t < 0 ? 0u : kv_bytes, kd, k_boff[u], toff);
+        buffer_load_lds16(kg, t < 0 ? 0u : k_bytes, kd, k_boff[u], toff);
     };
     auto load_v = [&](int t, int buf, int u) __attribute__((always_inline)) {
-        const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * D * 2;
-        lds_void* vd = (lds_void*)((buf ? v_lds1 : v_lds0) + (wave * KCH + u) * 64 * 8);
-        buffer_load_lds16(vg, t < 0 ? 0u : kv_bytes, vd, v_boff[u], toff);
+        const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * p.v_sl * 2;
+        lds_void* vd = (lds_void*)((buf ? v_lds1 : v_lds0) + (wave * KCHV + u) * 64 * 8);
+        buffer_load_lds16(vg, t < 0 ? 0u : v_bytes, vd, v_boff[u], toff);
     };
     auto issue_loads = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            load_k(t, buf, u);
-            load_v(t, buf, u);
-        }
+        for (int u = 0; u < KCH; ++u) load_k(t, buf, u);
+#pragma unroll
+        for (int u = 0; u < KCHV; ++u) load_v(t, buf, u);
     };
+
+    // additive mask of this slice: a buffer over rows [0, Lq) (row qrow, or
+    // the last row for rows past Lq); reads past its end return zeros, and
+    // keys past kv_len are masked anyway
+    const float* mg = MASK ? p.mask + b * p.m_sb + hh * p.m_sh : nullptr;
+    const uint32_t m_bytes = MASK ? (uint32_t)(((long long)(p.Lq - 1) * p.m_sl + p.Lk) * 4) : 0u;
+    const __amdgpu_buffer_rsrc_t mrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(mg), (short)0, (int)m_bytes, 0x00020000);
+    const uint32_t m_row_off = MASK ? (uint32_t)(qrow < p.Lq ? qrow : p.Lq - 1) * p.m_sl * 4 : 0u;
 
     f32x16 o[NDT];
 #pragma unroll
@@ -195,6 +217,34 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     auto tile_math = [&](auto FAST, int t, const uint16_t* Ks, const uint16_t* Vs, int lt,
                          int lb) __attribute__((always_inline)) {
         const int ts = t * BC;
+        // mask values of this lane's 16 keys per sub-tile (two runs of 8
+        // consecutive keys), fetched before the products so they arrive
+        // under them
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        f32x4 mb[MASK ? NKT : 1][4];
+        if constexpr (MASK) {
+            if (p.mask_vec) {   // 16-byte aligned rows: one 16-byte load per 4 keys
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int key = ts + kt * 32 + 16 * (j >> 1) + 8 * h + 4 * (j & 1);
+                        mb[kt][j] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(mrsrc, m_row_off + key * 4, 0, 0));
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int key = ts + kt * 32 + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + e;
+                            mb[kt][j][e] = __builtin_bit_cast(
+                                float, __builtin_amdgcn_raw_buffer_load_b32(mrsrc, m_row_off + key * 4, 0, 0));
+                        }
+            }
+        }
         // S^T = K Q^T, one 32-key sub-tile after the other so the softmax of
         // the first can start under the MFMAs of the second; operand reads
         // run one k-step ahead.
@@ -218,6 +268,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
             }
         }
 
+        // additive mask, in raw-score units (the weights take s * sl)
+        if constexpr (MASK) {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[kt][r] = __builtin_fmaf(mb[kt][r >> 2][r & 3], p.inv_scale, s[kt][r]);
+        }
         // masks: padding / ragged tail and the causal diagonal
         const bool need_mask = (ts + BC > kv_len) || (CAUSAL && ts + BC - 1 > q0w);
         if (need_mask) {
@@ -237,13 +295,13 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         constexpr int NSTEP = 2 * NKT;
         i16x8 va[3][NDT];
         auto read_v = [&](int step, i16x8* dst) __attribute__((always_inline)) {
-            const int roff = (step * 16) * D;   // step = 2*kt + ksl
+            const int roff = (step * 16) * DV;   // step = 2*kt + ksl
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_i16x4*)(Vs + roff + v_rd[dt]));
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(Vs + roff + 4 * D + v_rd[dt]));
+                    (lds_i16x4*)(Vs + roff + 4 * DV + v_rd[dt]));
                 dst[dt] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
         };
@@ -307,7 +365,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, va[st % 3][dt]), pb[st >> 1][st & 1], o[dt], 0, 0, 0);
 #pragma unroll
-            for (int u = st * KCH / NSTEP; u < (st + 1) * KCH / NSTEP; ++u) load_v(lt, lb, u);
+            for (int u = st * KCHV / NSTEP; u < (st + 1) * KCHV / NSTEP; ++u) load_v(lt, lb, u);
         }
     };
 
@@ -356,7 +414,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     const float l = sum_across_halves(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (qrow < p.Lq) {
-        uint16_t* dst = p.out + q_base + (size_t)qrow * D;
+        uint16_t* dst = p.out + b * p.o_sb + hh * p.o_sh + (size_t)qrow * p.o_sl;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -376,10 +434,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     }
 }
 
-template <int D, int BC, int NW, bool CAUSAL, bool LENS>
+template <int D, int DV, int BC, int NW, bool CAUSAL, bool LENS, bool MASK>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     constexpr int BR = NW * 32;
-    auto kern = fwd_bf16_kernel<D, BC, NW, CAUSAL, LENS>;
+    auto kern = fwd_bf16_kernel<D, DV, BC, NW, CAUSAL, LENS, MASK>;
     KParams p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -391,7 +449,17 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     p.Lq = a.Lq;
     p.Lk = a.Lk;
     p.num_qb = (a.Lq + BR - 1) / BR;
-    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const double scale = a.scale > 0.f ? (double)a.scale : 1.0 / sqrt((double)D);
+    p.scale_log2 = (float)(1.4426950408889634 * scale);
+    p.inv_scale = (float)(1.0 / scale);
+    p.q_sb = a.q_sb; p.q_sh = a.q_sh; p.q_sl = a.q_sl;
+    p.k_sb = a.k_sb; p.k_sh = a.k_sh; p.k_sl = a.k_sl;
+    p.v_sb = a.v_sb; p.v_sh = a.v_sh; p.v_sl = a.v_sl;
+    p.o_sb = a.o_sb; p.o_sh = a.o_sh; p.o_sl = a.o_sl;
+    p.mask = a.mask;
+    p.m_sb = a.m_sb; p.m_sh = a.m_sh; p.m_sl = a.m_sl;
+    p.mask_vec = a.mask != nullptr && reinterpret_cast<uintptr_t>(a.mask) % 16 == 0 && a.m_sb % 4 == 0 &&
+                 a.m_sh % 4 == 0 && a.m_sl % 4 == 0;
     const long long items = (long long)p.num_qb * a.B * a.H;
     if (items <= 0 || items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     p.num_items = (int)items;
@@ -405,12 +473,21 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int BC, int NW>
+template <int D, int DV, int BC, int NW, bool MASK>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
     const bool lens = a.key_lens != nullptr;
     if (a.causal)
-        return lens ? launch_one<D, BC, NW, true, true>(a, s) : launch_one<D, BC, NW, true, false>(a, s);
-    return lens ? launch_one<D, BC, NW, false, true>(a, s) : launch_one<D, BC, NW, false, false>(a, s);
+        return lens ? launch_one<D, DV, BC, NW, true, true, MASK>(a, s)
+                    : launch_one<D, DV, BC, NW, true, false, MASK>(a, s);
+    return lens ? launch_one<D, DV, BC, NW, false, true, MASK>(a, s)
+                : launch_one<D, DV, BC, NW, false, false, MASK>(a, s);
+}
+
+// default tiles (64 keys, 4 wavefronts) for every (d_k, d_v) pair, with and
+// without the additive mask
+template <int D, int DV>
+hipError_t launch_default(const FwdArgs& a, hipStream_t s) {
+    return a.mask != nullptr ? launch_d<D, DV, 64, 4, true>(a, s) : launch_d<D, DV, 64, 4, false>(a, s);
 }
 
 }  // namespace
@@ -419,11 +496,19 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s) {
     if (t.kind == 1) return launch_fwd_bf16_pipe(a, t, s);
     if (t.kind == 2) return launch_fwd_bf16_pp(a, t, s);
     if (t.kind == 3) return launch_fwd_bf16_wide(a, t, s);
-    if (t.d == 128 && t.bc == 64 && t.waves == 4) return launch_d<128, 64, 4>(a, s);
-    if (t.d == 128 && t.bc == 64 && t.waves == 8) return launch_d<128, 64, 8>(a, s);
-    if (t.d == 64 && t.bc == 64 && t.waves == 4) return launch_d<64, 64, 4>(a, s);
-    if (t.d == 64 && t.bc == 128 && t.waves == 4) return launch_d<64, 128, 4>(a, s);
-    if (t.d == 64 && t.bc == 64 && t.waves == 8) return launch_d<64, 64, 8>(a, s);
+    if (t.d != a.d) return hipErrorInvalidValue;
+    if (t.bc == 64 && t.waves == 4) {
+        if (a.d == 128 && a.dv == 128) return launch_default<128, 128>(a, s);
+        if (a.d == 128 && a.dv == 64) return launch_default<128, 64>(a, s);
+        if (a.d == 64 && a.dv == 64) return launch_default<64, 64>(a, s);
+        if (a.d == 64 && a.dv == 128) return launch_default<64, 128>(a, s);
+        return hipErrorInvalidValue;
+    }
+    // the other tiles: d_v = d_k, no mask
+    if (a.dv != a.d || a.mask != nullptr) return hipErrorInvalidValue;
+    if (t.d == 128 && t.bc == 64 && t.waves == 8) return launch_d<128, 128, 64, 8, false>(a, s);
+    if (t.d == 64 && t.bc == 128 && t.waves == 4) return launch_d<64, 64, 128, 4, false>(a, s);
+    if (t.d == 64 && t.bc == 64 && t.waves == 8) return launch_d<64, 64, 64, 8, false>(a, s);
     return hipErrorInvalidValue;
 }
 

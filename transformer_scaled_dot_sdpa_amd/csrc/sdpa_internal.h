@@ -7,8 +7,12 @@
 
 namespace sdpa {
 
-// Arguments shared by every forward kernel.  Tensors are contiguous
-// [B, H, L, d] (q/out with L = Lq, k/v with L = Lk); lse is [B, H, Lq].
+// Arguments shared by every forward kernel.  q/k/v/out are [B, H, L, width]
+// views (q/out with L = Lq, k/v with L = Lk; width d for q/k, dv for v/out)
+// given by element strides of batch, head and row; the last dimension is
+// contiguous.  lse is contiguous [B, H, Lq].  Only the main bf16 kernel and
+// the fp32 kernel honour strides, dv != d, scale and mask; the other bf16
+// kernels take the contiguous defaults (set_contiguous).
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -17,8 +21,29 @@ struct FwdArgs {
     float* lse;               // may be null
     const int32_t* key_lens;  // device int32[B], may be null
     int B, H, Lq, Lk, d;
+    int dv;
     int causal;
     int num_cus;              // compute units of the device (sizes persistent grids)
+    long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+    int q_sl, k_sl, v_sl, o_sl;
+    float scale;              // > 0: scores are q.k * scale; else 1/sqrt(d)
+    const float* mask;        // additive fp32 mask on the scaled scores, or null
+    long long m_sb, m_sh;     // mask strides (0 broadcasts)
+    int m_sl;
+
+    // contiguous [B, H, L, width] tensors, dv = d, default scale, no mask
+    void set_contiguous() {
+        dv = d;
+        q_sl = o_sl = k_sl = v_sl = d;
+        q_sh = o_sh = (long long)Lq * d;
+        k_sh = v_sh = (long long)Lk * d;
+        q_sb = o_sb = (long long)H * Lq * d;
+        k_sb = v_sb = (long long)H * Lk * d;
+        scale = 0.f;
+        mask = nullptr;
+        m_sb = m_sh = 0;
+        m_sl = 0;
+    }
 };
 
 // Arguments of the backward kernels.  Layouts as FwdArgs; dout, dq have q's
