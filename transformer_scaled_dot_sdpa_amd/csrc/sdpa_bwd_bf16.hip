@@ -371,17 +371,20 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BParams p) {
 
     // per-row statistics of a query tile (lse in exp2 units and D), loaded
     // by the first 128 threads into registers, stored to LDS before the
-    // barrier that opens the tile
+    // barrier that opens the tile.  The load is consumed only at the store:
+    // any arithmetic on it right after the load would make the wavefront
+    // wait for all its loads in flight, the next tile's included.
     float stat = 0.f;
+    const float stat_mul = tid < BQ ? kLog2e : 1.f;
     auto stat_load = [&](int t) __attribute__((always_inline)) {
         if (tid < 2 * BQ) {
             int row = t * BQ + (tid & (BQ - 1));
             row = row < p.Lq ? row : p.Lq - 1;
-            stat = tid < BQ ? lse_g[row] * kLog2e : dl_g[row];
+            stat = tid < BQ ? lse_g[row] : dl_g[row];
         }
     };
     auto stat_store = [&](int buf) __attribute__((always_inline)) {
-        if (tid < 2 * BQ) st_lds[buf][tid / BQ][tid & (BQ - 1)] = stat;
+        if (tid < 2 * BQ) st_lds[buf][tid / BQ][tid & (BQ - 1)] = stat * stat_mul;
     };
     auto issue_loads = [&](int t, uint16_t* qb, uint16_t* gb) __attribute__((always_inline)) {
         const uint32_t toff = (uint32_t)(t * BQ) * D * 2;
