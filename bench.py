@@ -214,14 +214,48 @@ def backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args, fwd_flops_alg)
     achieved = flops / (ms * 1e-3) / 1e12
     head = 2.5 * w.flops / (ms_wall * 1e-3) / 1e12
     print(f"[bench] backward {ms:.4f} ms/call, {achieved:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = backward_cpu_baseline(w, sets, dout, (dq, dk, dv), args.cpu_seconds / 2)
     del dq, dk, dv, delta, dout
-    return {"ms_per_call": ms, "ms_per_step_wall": ms_wall, "steps": steps,
+    out = {"ms_per_call": ms, "ms_per_step_wall": ms_wall, "steps": steps,
             "value": head, "unit": "TFLOP/s",
             "flops_note": "10*d_k per pair (2.5x the forward's 4*d_k), halved for causal",
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                          "algorithmic_flops_per_call": flops,
                          "kernels": "bwd_delta_kernel, bwd_dq_kernel, bwd_dkdv_kernel"}}
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    return out
+
+
+def backward_cpu_baseline(w, sets, dout, grads, target_s):
+    """The oracle's fp64 backward on whole (b, h) slices (one thread per
+    slice, as many slices as host threads, repeated up to the time target),
+    TFLOP/s at 10*d_k flops per valid pair; plus the largest gradient
+    difference against the GPU on the sample."""
+    import numpy as np
+    import oracle
+    threads = min(16, len(os.sched_getaffinity(0)))
+    nsl = min(threads, w.H)
+    bits = lambda t: t[0:1, 0:nsl].contiguous().cpu().view(torch_int16()).numpy().view(np.uint16)
+    tq, tk, tv = (bits(t) for t in sets[0][:3])
+    g = bits(dout)
+    t0 = time.perf_counter()
+    ref = oracle.sdpa_bwd(tq, tk, tv, g, causal=w.causal, bf16=True, nthreads=threads)
+    sec = time.perf_counter() - t0
+    pairs_per_slice = (w.Lq * (w.Lq + 1) // 2) if (w.causal and w.Lq == w.Lk) else w.Lq * w.Lk
+    flops = 10.0 * w.d * pairs_per_slice * nsl
+    diff = max(float(np.max(np.abs(gr[0:1, 0:nsl].float().cpu().numpy() - r))) for gr, r in zip(grads, ref))
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nsl} whole (b,h) slice(s) of {w.name}, fp64 backward, {sec:.2f} s wall",
+            "seconds": sec, "sample_max_abs_grad_vs_gpu": diff}
+
+
+def torch_int16():
+    import torch
+    return torch.int16
 
 
 def forward_ex_leg(torch, sdpa, w, sets, tkl, stream, args):
@@ -307,8 +341,21 @@ def decode_leg(torch, sdpa, inputs, name, args):
     gbs = bytes_alg / (dec_ms * 1e-3) / 1e9
     print(f"[bench] decode {w.name}: {dec_ms*1e3:.1f} us ({gbs:.0f} GB/s); forward on the same "
           f"inputs {fwd_ms*1e3:.1f} us", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = min(16, len(os.sched_getaffinity(0)))
+        sdpa.decode(tq, tk, tv, causal=w.causal, key_lens=tkl, out=out, lse=lse, workspace=ws,
+                    stream=stream)
+        dec_out = out.float().cpu().numpy()
+        t0 = time.perf_counter()
+        ro, rl = oracle.sdpa(q, k, v, causal=w.causal, key_lens=kl, bf16=True, nthreads=threads)
+        sec = time.perf_counter() - t0
+        cpu = {"value": bytes_alg / sec / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole {w.name} workload, fp64, {sec:.2f} s wall", "seconds": sec,
+               "sample_max_abs_out_vs_gpu": float(np.max(np.abs(dec_out - ro)))}
     del sets, out, lse, ws
-    return {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d_k": w.d,
+    res = {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d_k": w.d,
             "key_lens": None if kl is None else "uniform[%d,%d]" % w.key_lens,
             "input_sets": nsets, "steps": steps, "us_per_call": dec_ms * 1e3,
             "workspace_bytes": need,
@@ -316,6 +363,9 @@ def decode_leg(torch, sdpa, inputs, name, args):
                          "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_call": bytes_alg,
                          "kernels": "decode_kernel (+ decode_combine when split)"},
             "forward_same_inputs_us": fwd_ms * 1e3}
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    return res
 
 
 def main():
