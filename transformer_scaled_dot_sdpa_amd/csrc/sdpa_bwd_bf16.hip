@@ -61,6 +61,12 @@ struct BParams {
 };
 
 constexpr float kLog2e = 1.44269504088896340736f;
+// dK and dV in two passes (bwd_dkdv_kernel MODE 1 and 2) rather than one
+// when the single pass needs more registers than two wavefronts per SIMD
+// allow (d = 128; at d = 64 the single pass already runs two per SIMD and
+// is faster)
+template <int D>
+constexpr bool kSplitDkDv = D == 128;
 
 // ---------------------------------------------------------------- D
 template <int D>
@@ -304,8 +310,13 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <int D, bool CAUSAL, bool LENS>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BParams p) {
+// MODE 0: dK and dV in one pass (all four products; one wavefront per SIMD).
+// MODE 1: dV only (S, P, dV).  MODE 2: dK only (S, dP, dS, dK).  The two
+// single passes recompute S once more but need half the registers each, so
+// two wavefronts share every SIMD.
+template <int D, bool CAUSAL, bool LENS, int MODE>
+__global__ void __launch_bounds__(256, MODE == 0 ? 1 : 2) bwd_dkdv_kernel(BParams p) {
+    constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
     constexpr int BQ = 64, NT = 256, BK = 128;
     constexpr int CPR = D / 8;
     constexpr int KCH = BQ * CPR / NT;
@@ -364,7 +375,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BParams p) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             kf[ks] = __builtin_bit_cast(bf16x8, sk[2 * ks]);
-            vf[ks] = __builtin_bit_cast(bf16x8, sv[2 * ks]);
+            if constexpr (DO_DK) vf[ks] = __builtin_bit_cast(bf16x8, sv[2 * ks]);
         }
     }
     const bool key_ok = key < kv_len;
@@ -414,9 +425,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BParams p) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + qt * 32 * D + off.rd[ks]);
-                const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gs + qt * 32 * D + off.rd[ks]);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+                if constexpr (DO_DK) {
+                    const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Gs + qt * 32 * D + off.rd[ks]);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+                }
             }
             // accumulator r of lane (n, h) is query row qbase + 16(r/8) + 8h +
             // r%8 against key `key`
@@ -449,18 +462,20 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BParams p) {
                     if (CAUSAL) ok = ok && key <= qrow;
                     pv = ok ? pv : 0.f;
                 }
-                pb[r >> 3][r & 7] = (__bf16)pv;
-                sb[r >> 3][r & 7] = (__bf16)(pv * (dp[r] - dlv[r]));
+                if constexpr (DO_DV) pb[r >> 3][r & 7] = (__bf16)pv;
+                if constexpr (DO_DK) sb[r >> 3][r & 7] = (__bf16)(pv * (dp[r] - dlv[r]));
             }
             // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Gs, off, qt, st, dt), pb[st],
-                                                                      dva[dt], 0, 0, 0);
-                    dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Qs, off, qt, st, dt), sb[st],
-                                                                      dka[dt], 0, 0, 0);
+                    if constexpr (DO_DV)
+                        dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Gs, off, qt, st, dt),
+                                                                          pb[st], dva[dt], 0, 0, 0);
+                    if constexpr (DO_DK)
+                        dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Qs, off, qt, st, dt),
+                                                                          sb[st], dka[dt], 0, 0, 0);
                 }
         }
     };
@@ -507,8 +522,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BParams p) {
                     wk[c] = (__bf16)(dka[dt][4 * g4 + c] * p.scale);
                     wv[c] = (__bf16)dva[dt][4 * g4 + c];
                 }
-                *reinterpret_cast<uint2*>(dstk + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wk);
-                *reinterpret_cast<uint2*>(dstv + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wv);
+                if constexpr (DO_DK)
+                    *reinterpret_cast<uint2*>(dstk + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wk);
+                if constexpr (DO_DV)
+                    *reinterpret_cast<uint2*>(dstv + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wv);
             }
     }
     __syncthreads();
@@ -564,8 +581,17 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         p.num_items = (int)items;
         p.upi = CAUSAL ? 2 : 1;
         p.num_units = (int)((items + p.upi - 1) / p.upi);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, LENS>), dim3((unsigned)p.num_units), dim3(256), 0,
-                           stream, p);
+        if constexpr (kSplitDkDv<D>) {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, LENS, 1>), dim3((unsigned)p.num_units), dim3(256), 0,
+                               stream, p);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, LENS, 2>), dim3((unsigned)p.num_units), dim3(256), 0,
+                               stream, p);
+        } else {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, LENS, 0>), dim3((unsigned)p.num_units), dim3(256), 0,
+                               stream, p);
+        }
         return hipGetLastError();
     }
 }
