@@ -463,11 +463,14 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     const long long items = (long long)p.num_qb * a.B * a.H;
     if (items <= 0 || items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     p.num_items = (int)items;
-    p.upi = CAUSAL ? 2 : 1;
-    p.num_units = (int)((items + p.upi - 1) / p.upi);
     // one unit per workgroup: the hardware hands units to free slots as they
-    // come, which balances better than a fixed assignment; causal units are
-    // long/short pairs of equal length
+    // come, which balances better than a fixed assignment.  Causal units are
+    // long/short pairs of equal length once there are more items than
+    // resident workgroups; a smaller problem takes one item per workgroup so
+    // that every item starts at once.
+    const long long slots = (long long)(a.num_cus > 0 ? a.num_cus : 256) * (8 / NW);
+    p.upi = (CAUSAL && items > slots) ? 2 : 1;
+    p.num_units = (int)((items + p.upi - 1) / p.upi);
     const long long nwg = p.num_units;
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
