@@ -91,8 +91,9 @@ sdpa_status_t sdpa_create(sdpa_handle_t* h, sdpa_dtype_t dtype, int device);
  * Errors (returned before anything is enqueued; out and lse untouched):
  * INVALID_VALUE for a NULL handle or tensor pointer, sizes < 1, causal not
  * 0/1, overlapping out, or sizes whose element counts overflow int64;
- * NOT_SUPPORTED for d_k outside the handle dtype's range or bf16 pointers
- * not 16-byte aligned; HIP_ERROR if the launch fails.  Faults during
+ * NOT_SUPPORTED for d_k outside the handle dtype's range, bf16 pointers
+ * not 16-byte aligned, or a bf16 (b, h) slice of k or v of 4 GiB or more
+ * (Lk * d_k * 2 >= 2^32); HIP_ERROR if the launch fails.  Faults during
  * execution surface at the caller's next synchronisation, as in HIP.
  */
 sdpa_status_t sdpa_forward(sdpa_handle_t h,
@@ -206,8 +207,9 @@ sdpa_status_t sdpa_forward_ex(sdpa_handle_t h, const sdpa_forward_desc_t* desc, 
  * causal not 0/1, element counts overflowing int64, misaligned float
  * pointers, or any written buffer (delta, dq, dk, dv) overlapping another
  * argument; NOT_SUPPORTED for d_k outside the handle dtype's range (bf16:
- * 64 or 128) or bf16 pointers not 16-byte aligned; HIP_ERROR if a launch
- * fails.
+ * 64 or 128), bf16 pointers not 16-byte aligned, or a bf16 (b, h) slice of
+ * 4 GiB or more (Lq * d_k * 2 or Lk * d_k * 2 >= 2^32); HIP_ERROR if a
+ * launch fails.
  */
 sdpa_status_t sdpa_backward(sdpa_handle_t h,
                             const void* q, const void* k, const void* v,

@@ -115,3 +115,32 @@ def test_backward_validation_statuses_on_gpu():
     assert bwd(d_k=96) == b.NOT_SUPPORTED
     assert bwd(d_k=64, dv=p(t["dv"]) + 2) == b.NOT_SUPPORTED   # misaligned bf16
     assert bwd(B=1 << 30, H=1 << 30) == b.INVALID_VALUE
+
+
+
+@pytest.mark.gpu
+def test_bf16_slices_of_4gib_rejected():
+    """bf16 kernels address one (b, h) slice with 32-bit byte offsets: a key
+    slice of 2^32 bytes or more is refused before any launch.  The tensors
+    are real allocations of that size (k doubles as v), so no access could
+    leave them either way."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    h = b.handle_for(b.DTYPE_BF16, 0)
+    d, Lq, Lk = 128, 64, (1 << 24) + 64        # Lk * d * 2 = 2^32 + 16 KiB
+    p = lambda t: t.data_ptr()
+    small = lambda: torch.zeros(1, 1, Lq, d, dtype=torch.bfloat16, device="cuda")
+    big = lambda: torch.empty(1, 1, Lk, d, dtype=torch.bfloat16, device="cuda")
+    q, out, dout, dq = small(), small(), small(), small()
+    kv = big()
+    assert b.sdpa_forward(h, p(q), p(kv), p(kv), p(out), None, 1, 1, Lq, Lk, d, 0, None,
+                          None) == b.NOT_SUPPORTED
+    with pytest.raises(b.SdpaError):
+        b.forward_ex(q, kv, kv)
+    lse = torch.zeros(1, 1, Lq, device="cuda")
+    delta = torch.zeros_like(lse)
+    dk, dv = big(), big()
+    assert b.sdpa_backward(h, p(q), p(kv), p(kv), p(out), p(dout), p(lse), p(delta), p(dq), p(dk),
+                           p(dv), 1, 1, Lq, Lk, d, 0, None, None) == b.NOT_SUPPORTED
+    torch.cuda.synchronize()

@@ -65,6 +65,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                 raise RuntimeError(
                     f"HIP library not found at {path}; build it with "
                     "`python -m transformer_scaled_dot_sdpa_amd.build`")
+            # torch ships its own HIP runtime under the soname the library
+            # links against.  Loaded first, that runtime also serves the
+            # library; loaded second, it would come in as another copy of
+            # the runtime beside the system one the library pulled in, and
+            # the two would not share devices.
+            try:
+                import torch  # noqa: F401
+            except ImportError:
+                pass
             lib = ctypes.CDLL(path)
             vp, i32 = ctypes.c_void_p, ctypes.c_int
             lib.sdpa_create.argtypes = [ctypes.POINTER(vp), i32, i32]

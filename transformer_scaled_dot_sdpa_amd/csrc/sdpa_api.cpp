@@ -162,6 +162,8 @@ sdpa_status_t sdpa_forward(sdpa_handle_t h, const void* q, const void* k, const 
             return SDPA_STATUS_NOT_SUPPORTED;
         for (const void* p : {q, k, v, (const void*)out})
             if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return SDPA_STATUS_NOT_SUPPORTED;
+        // buffer loads address a (b, h) slice of k and v with 32-bit offsets
+        if ((long long)Lk * d_k * 2 >= (1LL << 32)) return SDPA_STATUS_NOT_SUPPORTED;
     } else {
         if (d_k > 256) return SDPA_STATUS_NOT_SUPPORTED;
         for (const void* p : {q, k, v, (const void*)out})
@@ -224,6 +226,10 @@ sdpa_status_t sdpa_backward(sdpa_handle_t h, const void* q, const void* k, const
         if (d_k != 64 && d_k != 128) return SDPA_STATUS_NOT_SUPPORTED;
         for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
             if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return SDPA_STATUS_NOT_SUPPORTED;
+        // buffer loads address a (b, h) slice of q, dO (dK/dV pass) and k, v
+        // (dQ pass) with 32-bit offsets
+        if ((long long)Lq * d_k * 2 >= (1LL << 32) || (long long)Lk * d_k * 2 >= (1LL << 32))
+            return SDPA_STATUS_NOT_SUPPORTED;
     } else {
         if (d_k > 256) return SDPA_STATUS_NOT_SUPPORTED;
         for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
