@@ -106,6 +106,20 @@ def test_bf16_edges(d, case):
                 assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
 
 
+@pytest.mark.parametrize("d,kl", [(64, None), (128, [300, 150, 7])], ids=["d64", "d128-lens"])
+def test_bf16_causal_work_pairs(d, kl):
+    """A causal problem with more items (128-row query blocks x slices) than
+    resident workgroups runs as long/short pairs of items per workgroup.
+    Three blocks per slice make pairs that span two slices, and the odd item
+    count leaves a last unit of one item."""
+    B, H, L = 3, 65, 300          # 3 blocks x 195 slices = 585 items
+    seed = 4100 + d
+    announce(f"bf16 causal pairs d{d} B{B} H{H} L{L} key_lens={kl} seed={seed}")
+    q, k, v, _ = generate(B, H, L, L, d, "bf16", seed)
+    o, l = run_gpu(q, k, v, "bf16", True, kl)
+    ro, rl = oracle_ref(q, k, v, "bf16", True, kl)
+    assert_close(o, l, ro, rl, "bf16", f"causal pairs d{d}")
+
 EDGE_F32 = [
     # B, H, Lq, Lk, d, causal, key_lens
     (1, 2, 8, 8, 3, False, None),
