@@ -1,151 +1,94 @@
 // Ping-pong variant of the fused bf16 attention forward for gfx950.
 //
-// Same mathematics, layouts and masking as sdpa_fwd_bf16.hip (eq. (1) of
-// "Aufmerksamkeit ist alles, was Sie brauchen", section 3.2.1, with the
-// online softmax justified by the ratio identity of the formula page
-// "トランスフォーマーの注意機構", section 証明).  What differs is how the two
-// wavefronts that share a SIMD are phased.
+// Same mathematics, operand layouts, LDS layouts and masking as
+// sdpa_fwd_bf16.hip: eq. (1) of "Aufmerksamkeit ist alles, was Sie
+// brauchen", section 3.2.1, with the running maximum and sum justified by
+// the ratio identity of the formula page "トランスフォーマーの注意機構",
+// section 証明.  What differs is how the two wavefronts that share a SIMD are
+// phased.
 //
-// A workgroup has 8 wavefronts (256 query rows); wavefronts w and w + 4 run
-// on the same SIMD.  Group A (waves 0..3) and group B (waves 4..7) do the
-// same per-tile work -- S = K Q^T on the matrix cores, then the softmax on
-// the vector ALU and O += P V on the matrix cores -- but B runs one phase
-// behind A, phases being separated by workgroup barriers:
+// A workgroup has 8 wavefronts (256 query rows, one workgroup per CU);
+// wavefronts w and w + 4 run on the same SIMD.  Each wavefront alternates
+// between two kinds of step:
+//     M(t)   matrix step: O += P(t - 1) V(t - 1), then S(t) = K(t) Q^T
+//            (32 MFMAs at d_k = 128, no vector arithmetic);
+//     SM(t)  vector step: the softmax of S(t) into bf16 weights P(t)
+//            (no MFMA).
+// Group A (wavefronts 0..3) and group B (4..7) run the same sequence, B one
+// step behind A, with a workgroup barrier between steps:
+//     phase 2t     A: M(t)      B: SM(t - 1)
+//     phase 2t + 1 A: SM(t)     B: M(t)
+// so in every phase one wavefront of each SIMD has only matrix work and the
+// other only vector work.  Query blocks of 32 rows alternate between the
+// groups (A: 0, 2, 4, 6; B: 1, 3, 5, 7), so on a causal diagonal both groups
+// run out of keys at about the same tile.
 //
-//     phase 2t   : A computes S(t)                B does softmax + P.V (t-1)
-//     phase 2t+1 : A does softmax + P.V (t)       B computes S(t)
+// K and V tiles are triple buffered; each phase issues one batch of loads,
+// and a barrier leaves the last two phases' batches in flight (the schedule
+// is spelled out at run_pass).  The barriers carry no memory fence.
 //
-// so in every phase one wave of each SIMD keeps the matrix cores busy while
-// the other one's vector work runs beside it.  Query blocks of 32 rows
-// alternate between the groups (A: 0, 2, 4, 6; B: 1, 3, 5, 7), so on a causal
-// diagonal both groups stop at about the same tile.
-//
-// Both groups run the same sequence -- S(t), barrier, softmax + P.V (t),
-// barrier -- and B enters it through one extra barrier (A leaves through
-// one at the end), which puts B exactly one phase behind A.
-//
-// LDS: K and V tiles of 64 keys, two buffers each (64 KiB).  Group A issues
-// all loads: K(t+1) as it starts S(t), V(t+1) as it starts softmax + P.V (t);
-// at each barrier A waits for every batch but the one it issued in that
-// phase, so a batch has two phases to arrive.
+// Measured on the large causal d_k = 128 workload this variant is slower
+// than the default kernel: a matrix step takes about 1900 cycles for its 32
+// MFMAs (1024 cycles of matrix work), because only the four wavefronts in
+// their matrix step read LDS at a time, and the two transposed 8-byte V
+// reads per P.V product then limit the rate.  It stays selectable for
+// comparison.
 #include "sdpa_internal.h"
 #include "bf16_common.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace sdpa {
 namespace {
 
 using namespace bf16k;
 
-// s_waitcnt immediates: vmcnt = N, expcnt and lgkmcnt at max (no wait).
-template <int N>
-constexpr int wait_vmcnt() {
-    return (N & 0xF) | ((N >> 4) << 14) | 0x0F70;
-}
-
 template <int D, bool CAUSAL, bool LENS>
 __global__ void __launch_bounds__(512, 1) fwd_bf16_pp_kernel(KParams p) {
     constexpr int NW = 8;
-    constexpr int BC = 64;
     constexpr int NT = NW * 64;
-    constexpr int BR = NW * 32;
-    constexpr int CPR = D / 8;
-    constexpr int KCH = BC * CPR / (NT / 2);   // 16-byte loads per group-A thread per tile
+    constexpr int BR = NW * 32;                // 256 query rows
+    constexpr int BC = 64;                     // keys per tile
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int KCH = BC * CPR / NT;         // 16-byte loads per thread per K (or V) tile
     constexpr int TILE = BC * D;
     constexpr int NKT = BC / 32;
     constexpr int NDT = D / 32;
     constexpr int NKS = D / 16;
-    static_assert((BC * CPR) % (NT / 2) == 0, "tile must split evenly over group A");
+    static_assert((BC * CPR) % NT == 0, "tile must split evenly over threads");
+    static_assert(2 * KCH < 16, "vmcnt immediate below");
+    // s_waitcnt immediate: vmcnt = 2 KCH (the loads of the last two phases
+    // stay in flight), expcnt and lgkmcnt at their maximum (no wait)
+    constexpr int kWaitPhase = 0x0F70 | (2 * KCH);
 
-    extern __shared__ __align__(16) uint16_t smem[];  // K[0], K[1], V[0], V[1]
-
-    int bh, qb;
-    map_workgroup<CAUSAL>(p.num_qb, &bh, &qb);
-    const int b = bh / p.H;
-    const int q0 = qb * BR;
+    // three K and three V buffers (tile t in buffer t % 3), in separate
+    // arrays so that the compiler sees the loads into one buffer never alias
+    // the reads of another and adds no waits for them
+    __shared__ __align__(16) uint16_t k_lds0[TILE], k_lds1[TILE], k_lds2[TILE];
+    __shared__ __align__(16) uint16_t v_lds0[TILE], v_lds1[TILE], v_lds2[TILE];
+    auto k_buf = [&](int i) __attribute__((always_inline)) { return i == 0 ? k_lds0 : i == 1 ? k_lds1 : k_lds2; };
+    auto v_buf = [&](int i) __attribute__((always_inline)) { return i == 0 ? v_lds0 : i == 1 ? v_lds1 : v_lds2; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int group = wave >> 2;                        // 0 = A, 1 = B
-    const int blk = 2 * (wave & 3) + group;             // 32-row block of this wave
+    const int group = wave >> 2;               // 0: A; 1: B, one phase behind
+    const int blk = 2 * (wave & 3) + group;    // this wavefront's 32-row block
     const int n = lane & 31;
     const int h = lane >> 5;
 
-    int kv_len = p.Lk;
-    if (LENS) {
-        int L = p.key_lens[b];
-        L = L < 0 ? 0 : L;
-        kv_len = L < kv_len ? L : kv_len;
-    }
-    const int kv_end = CAUSAL ? min(kv_len, q0 + BR) : kv_len;
-    const int ntiles = (kv_end + BC - 1) / BC;
-
-    const int q0w = q0 + blk * 32;
-    const int qrow = q0w + n;
-    const int wave_kv_end = CAUSAL ? min(kv_len, q0w + 32) : kv_len;
-
-    const size_t q_base = (size_t)bh * p.Lq * D;
-    const uint16_t* kg = p.k + (size_t)bh * p.Lk * D;
-    const uint16_t* vg = p.v + (size_t)bh * p.Lk * D;
-
-    bf16x8 qf[NKS];
-    {
-        const int qr = qrow < p.Lq ? qrow : p.Lq - 1;
-        const i16x8* src = reinterpret_cast<const i16x8*>(p.q + q_base + (size_t)qr * D + 8 * h);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
-    }
-
-    // direct global -> LDS loads by group A (layout as in sdpa_fwd_bf16.hip)
-    const int wl = wave & 3;
+    // load u of this thread fills LDS slot (wave*KCH + u)*64 + lane of a tile
     uint32_t k_boff[KCH], v_boff[KCH];
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        const int s = (wl * KCH + u) * 64 + lane;
+        const int s = (wave * KCH + u) * 64 + lane;
         const int row = s / CPR, pc = s % CPR;
-        k_boff[u] = (k_lds_row(row) * D + ((pc ^ k_swz<D>(row)) << 3)) * 2;
-        v_boff[u] = (row * D + ((pc ^ v_swz<D>(row)) << 3)) * 2;
+        k_boff[u] = (k_lds_row(row) * p.k_sl + ((pc ^ k_swz<D>(row)) << 3)) * 2;
+        v_boff[u] = (row * p.v_sl + ((pc ^ v_swz<D>(row)) << 3)) * 2;
     }
-    // returns whether loads were issued
-    auto issue = [&](const uint16_t* gbase, const uint32_t* boff, int t,
-                     uint16_t* lds_tile) __attribute__((always_inline)) -> bool {
-        if (t >= ntiles) return false;
-        const int ts = t * BC;
-        const char* src = reinterpret_cast<const char*>(gbase + (size_t)ts * D);
-        lds_void* dst = (lds_void*)(lds_tile + wl * KCH * 64 * 8);
-        if (ts + BC <= kv_len) {
-#pragma unroll
-            for (int u = 0; u < KCH; ++u)
-                __builtin_amdgcn_global_load_lds((const void*)(src + boff[u]),
-                                                 (lds_void*)((char*)dst + u * 1024), 16, 0, 0);
-        } else {
-            const int last = kv_len - 1 - ts;
-#pragma unroll
-            for (int u = 0; u < KCH; ++u) {
-                const int r = (int)boff[u] / (2 * D), c = (int)boff[u] - r * 2 * D;
-                const uint32_t off = (uint32_t)((r < last ? r : last) * 2 * D + c);
-                __builtin_amdgcn_global_load_lds((const void*)(src + off),
-                                                 (lds_void*)((char*)dst + u * 1024), 16, 0, 0);
-            }
-        }
-        return true;
-    };
-    // phase barrier.  Group A first waits for all of its loads except the
-    // batch it issued in this phase (if it issued one); B only synchronises.
-    auto phase_barrier = [&](bool issued_now) __attribute__((always_inline)) {
-        if (group == 0) {
-            if (issued_now)
-                __builtin_amdgcn_s_waitcnt(wait_vmcnt<KCH>());
-            else
-                __builtin_amdgcn_s_waitcnt(wait_vmcnt<0>());
-        }
-        __syncthreads();
-    };
-    uint16_t* const Kb[2] = {smem, smem + TILE};
-    uint16_t* const Vb[2] = {smem + 2 * TILE, smem + 3 * TILE};
-
+    // per-lane LDS read offsets (elements), as in the main kernel
     int k_rd[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) k_rd[ks] = n * D + (((2 * ks + h) ^ k_swz<D>(n)) << 3);
@@ -161,51 +104,91 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_pp_kernel(KParams p) {
         }
     }
 
+    int unit_first, unit_step, unit_last;
+    workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
+    for (int unit = unit_first; unit < unit_last; unit += unit_step)
+    for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
+    int bh, qb;
+    item_block<CAUSAL>(item, p.num_qb, &bh, &qb);
+    const int b = bh / p.H;
+    const int hh = bh - b * p.H;
+    const int q0 = qb * BR;
+
+    int kv_len = p.Lk;
+    if (LENS) {
+        int L = p.key_lens[b];
+        L = L < 0 ? 0 : L;
+        kv_len = L < kv_len ? L : kv_len;
+    }
+    const int kv_end = CAUSAL ? min(kv_len, q0 + BR) : kv_len;
+    const int ntiles = (kv_end + BC - 1) / BC;
+
+    const int q0w = q0 + blk * 32;
+    const int qrow = q0w + n;
+    const int wave_kv_end = CAUSAL ? min(kv_len, q0w + 32) : kv_len;
+
+    const uint16_t* qg = p.q + b * p.q_sb + hh * p.q_sh;
+    const uint16_t* kg = p.k + b * p.k_sb + hh * p.k_sh;
+    const uint16_t* vg = p.v + b * p.v_sb + hh * p.v_sh;
+
+    bf16x8 qf[NKS];
+    {
+        const int qr = qrow < p.Lq ? qrow : p.Lq - 1;
+        const i16x8* src = reinterpret_cast<const i16x8*>(qg + (size_t)qr * p.q_sl + 8 * h);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
+    }
+
+    const uint32_t k_bytes = (uint32_t)kv_len * p.k_sl * 2;
+    const uint32_t v_bytes = (uint32_t)kv_len * p.v_sl * 2;
+    // loads of tile t into buffer buf; t < 0: zero-length loads (nothing is
+    // read; zeros land in a buffer no wavefront reads any more)
+    auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
+        const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * p.k_sl * 2;
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            lds_void* dst = (lds_void*)(k_buf(buf) + (wave * KCH + u) * 64 * 8);
+            buffer_load_lds16(kg, t < 0 ? 0u : k_bytes, dst, k_boff[u], toff);
+        }
+    };
+    auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
+        const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * p.v_sl * 2;
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            lds_void* dst = (lds_void*)(v_buf(buf) + (wave * KCH + u) * 64 * 8);
+            buffer_load_lds16(vg, t < 0 ? 0u : v_bytes, dst, v_boff[u], toff);
+        }
+    };
+
     f32x16 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    f32x16 s[NKT];
     float m_run = -INFINITY;
     float l_run = 0.f;
+    bool big = false;
     const float sl = p.scale_log2;
+    f32x16 s[NKT];   // the scores of a tile, from its S step to its SMPV step
 
-    // S^T = K Q^T for the whole 64-key tile (k-steps outermost, operand
-    // reads one k-step ahead)
-    auto s_phase = [&](const uint16_t* Ks) __attribute__((always_inline)) {
+    // S(t): S^T = K Q^T, then the key-length and causal masks
+    auto do_s = [&](int t, const uint16_t* Ks) __attribute__((always_inline)) {
+        const int ts = t * BC;
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+        for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-        bf16x8 ka[2][NKT];
+            bf16x8 ka[2];
+            ka[0] = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[0]);
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-            ka[0][kt] = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[0]);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (ks + 1 < NKS) {
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-                    ka[(ks + 1) & 1][kt] =
-                        *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[ks + 1]);
+            for (int ks = 0; ks < NKS; ++ks) {
+                if (ks + 1 < NKS)
+                    ka[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + k_rd[ks + 1]);
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1], qf[ks], s[kt], 0, 0, 0);
             }
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kt], qf[ks], s[kt], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, NKT, 0);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (ks + 1 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, NKT, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, NKT, 0);
-        }
-    };
-
-    // masks, online softmax and O^T += V^T P^T for tile t
-    auto smpv_phase = [&](int t, const uint16_t* Vs) __attribute__((always_inline)) {
-        const int ts = t * BC;
-        if ((ts + BC > kv_len) || (CAUSAL && ts + BC - 1 > q0w)) {
+        const bool need_mask = (ts + BC > kv_len) || (CAUSAL && ts + BC - 1 > q0w);
+        if (need_mask) {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -216,33 +199,60 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_pp_kernel(KParams p) {
                     s[kt][r] = ok ? s[kt][r] : -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+    };
+
+    bf16x8 pb[NKT][2];   // the bf16 weights of a tile, from its softmax to its P.V
+
+    // SM(t): weights from the scores of S(t).  fast: exponentials against
+    // the fixed reference m_run (set exactly by the first tile), recording
+    // only whether a tile's weights reached 2^64; otherwise the exact running
+    // maximum (rescaling O, which then holds the tiles before t only).
+    auto do_sm = [&](bool fast) __attribute__((always_inline)) {
+        if (fast) {
+            float lsum = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mt = mx * sl;
-        if (__ballot(mt > m_run + kRescaleSlack) != 0ull) {
-            const float mn = fmaxf(m_run, mt);
-            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
-            l_run *= alpha;
+                for (int r = 0; r < 16; ++r) {
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -m_run));
+                    lsum += pv;
+                    pb[kt][r >> 3][r & 7] = (__bf16)pv;
+                }
+            l_run += lsum;
+            big |= !(lsum < 0x1p64f);
+        } else {
+            float mx = -INFINITY;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            m_run = mn;
-        }
-        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-        bf16x8 pb[NKT][2];
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+            mx = max_across_halves(mx);
+            const float mt = mx * sl;
+            if (__ballot(mt > m_run + kRescaleSlack) != 0ull) {
+                const float mn = fmaxf(m_run, mt);
+                const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+                l_run *= alpha;
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+                for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -mref));
-                l_run += pv;
-                pb[kt][r >> 3][r & 7] = (__bf16)pv;
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                m_run = mn;
             }
+            const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -mref));
+                    l_run += pv;
+                    pb[kt][r >> 3][r & 7] = (__bf16)pv;
+                }
+        }
+    };
+
+    // PV: O^T += V^T P^T with the weights of the last softmax; the
+    // transposed V reads run one key step ahead
+    auto do_pv = [&](const uint16_t* Vs) __attribute__((always_inline)) {
         constexpr int NSTEP = 2 * NKT;
         i16x8 va[2][NDT];
         auto read_v = [&](int step, i16x8* dst) __attribute__((always_inline)) {
@@ -265,59 +275,111 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_pp_kernel(KParams p) {
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, va[st & 1][dt]), pb[st >> 1][st & 1], o[dt], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 1);
-#pragma unroll
-        for (int st = 0; st < NSTEP; ++st) {
-            if (st + 1 < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, NDT, 1);
-        }
     };
 
-    // phase work of this wave: S(t) from K buffer t&1, or softmax + P.V (t)
-    // from V buffer t&1 -- only for tiles that hold keys of this wave
-    auto do_s = [&](int t, const uint16_t* Ks) __attribute__((always_inline)) {
-        if (t >= 0 && t < ntiles && t * BC < wave_kv_end) s_phase(Ks);
-    };
-    auto do_smpv = [&](int t, const uint16_t* Vs) __attribute__((always_inline)) {
-        if (t >= 0 && t < ntiles && t * BC < wave_kv_end) smpv_phase(t, Vs);
+    auto phase_barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitPhase);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
 
-    if (ntiles > 0) {
-        const bool isA = group == 0;
-        if (isA) {
-            issue(kg, k_boff, 0, Kb[0]);
-            issue(vg, v_boff, 0, Vb[0]);
-        }
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt<0>());
+    // One pass over the tiles.  Per wavefront the work alternates between
+    // a matrix step M(t) = P(t-1).V(t-1) then S(t) (up to 32 MFMAs, no
+    // vector work) and a vector step SM(t) = the softmax of S(t) (no MFMA);
+    // M(ntiles) is the last P.V alone.  The phases (P = 2 ntiles + 2, with
+    // a barrier between consecutive ones) are numbered globally: A runs
+    // M(t) in phase 2t and SM(t) in phase 2t + 1; B one phase later.  So in
+    // every phase each SIMD holds one wavefront in a matrix step and one in
+    // a vector step.
+    // Loads: phase ph issues one batch per thread, V(ph/2 + 1) for even ph
+    // and K((ph + 3)/2) for odd ph, into buffer (tile % 3).  A barrier waits
+    // for all but the last two phases' batches.  K(t) goes out in phase
+    // 2t - 3 and V(t) in 2t - 2, at least two phases before the barrier
+    // that opens their first reader (A's M(t), phase 2t; A's M(t + 1),
+    // phase 2t + 2), and each refills a buffer whose last reader (B's
+    // M(t - 2) for K(t - 3), B's M(t - 2) for V(t - 3)) finished before.
+    // Each group runs its own copy of the loop, unrolled by three tiles so
+    // that every buffer is a compile-time choice.  all_exact: the exact
+    // softmax on every tile (the re-run after an overflow).
+    auto run_pass = [&](bool all_exact) __attribute__((always_inline)) {
+        auto tile = [&](int t) __attribute__((always_inline)) { return t < ntiles ? t : -1; };
+        issue_k(0, 0);
+        issue_v(0, 0);
+        issue_k(tile(1), 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        if (!isA) __syncthreads();   // B runs one phase behind A
-        bool iss;
-        for (int t = 0;; t += 2) {
-            // tile t: buffers 0
-            iss = isA && issue(kg, k_boff, t + 1, Kb[1]);
-            do_s(t, Kb[0]);
-            phase_barrier(iss);
-            iss = isA && issue(vg, v_boff, t + 1, Vb[1]);
-            do_smpv(t, Vb[0]);
-            if (t + 1 >= ntiles) break;
-            phase_barrier(iss);
-            // tile t + 1: buffers 1
-            iss = isA && issue(kg, k_boff, t + 2, Kb[0]);
-            do_s(t + 1, Kb[1]);
-            phase_barrier(iss);
-            iss = isA && issue(vg, v_boff, t + 2, Vb[0]);
-            do_smpv(t + 1, Vb[1]);
-            if (t + 2 >= ntiles) break;
-            phase_barrier(iss);
+        auto live = [&](int t) __attribute__((always_inline)) {
+            return t >= 0 && t < ntiles && t * BC < wave_kv_end;
+        };
+        // M(t) with tile t in buffers j (K) and tile t - 1 in buffer (j + 2) % 3 (V)
+        auto mstep = [&](int t, int j) __attribute__((always_inline)) {
+            if (live(t - 1)) do_pv(v_buf((j + 2) % 3));
+            if (live(t)) do_s(t, k_buf(j));
+        };
+        auto smstep = [&](int t) __attribute__((always_inline)) {
+            if (live(t)) do_sm(!all_exact && t > 0);
+        };
+        if (group == 0) {
+            // A: M(t) in phase 2t (loads V(t + 1)), SM(t) in phase 2t + 1
+            // (loads K(t + 2)); a barrier after each (the last phase,
+            // 2 ntiles + 1, has nothing left to do)
+            for (int t0 = 0; t0 <= ntiles; t0 += 3) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const int t = t0 + j;
+                    if (j > 0 && t > ntiles) break;
+                    issue_v(tile(t + 1), (j + 1) % 3);
+                    mstep(t, j);
+                    phase_barrier();
+                    if (t == ntiles) break;
+                    issue_k(tile(t + 2), (j + 2) % 3);
+                    smstep(t);
+                    phase_barrier();
+                }
+            }
+        } else {
+            // B: phase 0 only loads; M(t) in phase 2t + 1 (loads K(t + 2)),
+            // SM(t) in phase 2t + 2 (loads V(t + 2)); no barrier after the
+            // last phase
+            issue_v(tile(1), 1);
+            phase_barrier();
+            for (int t0 = 0; t0 <= ntiles; t0 += 3) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const int t = t0 + j;
+                    if (j > 0 && t > ntiles) break;
+                    issue_k(tile(t + 2), (j + 2) % 3);
+                    mstep(t, j);
+                    if (t == ntiles) break;
+                    phase_barrier();
+                    issue_v(tile(t + 2), (j + 2) % 3);
+                    smstep(t);
+                    phase_barrier();
+                }
+            }
         }
-        if (isA) __syncthreads();    // pairs with B's extra barrier
+        // zero-length loads of the last phases may still be in flight
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    };
+    if (ntiles > 0) {
+        run_pass(false);
+        if (__syncthreads_or(big)) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+            m_run = -INFINITY;
+            l_run = 0.f;
+            run_pass(true);
+        }
     }
 
     // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l)
-    const float l = l_run + __shfl_xor(l_run, 32);
+    const float l = sum_across_halves(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (qrow < p.Lq) {
-        uint16_t* dst = p.out + q_base + (size_t)qrow * D;
+        uint16_t* dst = p.out + b * p.o_sb + hh * p.o_sh + (size_t)qrow * p.o_sl;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -331,12 +393,15 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_pp_kernel(KParams p) {
         if (p.lse != nullptr && h == 0)
             p.lse[(size_t)bh * p.Lq + qrow] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
     }
+    // every wavefront is done with both LDS buffers before the next item's
+    // first loads overwrite them
+    __syncthreads();
+    }
 }
 
 template <int D, bool CAUSAL, bool LENS>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     constexpr int BR = 256;
-    const size_t lds = 4 * (size_t)64 * D * sizeof(uint16_t);
     KParams p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -348,10 +413,26 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     p.Lq = a.Lq;
     p.Lk = a.Lk;
     p.num_qb = (a.Lq + BR - 1) / BR;
-    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const long long nwg = (long long)p.num_qb * a.B * a.H;
-    if (nwg <= 0 || nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, LENS>), dim3((unsigned)nwg), dim3(512), lds,
+    const double scale = a.scale > 0.f ? (double)a.scale : 1.0 / sqrt((double)D);
+    p.scale_log2 = (float)(1.4426950408889634 * scale);
+    p.inv_scale = (float)(1.0 / scale);
+    p.q_sb = a.q_sb; p.q_sh = a.q_sh; p.q_sl = a.q_sl;
+    p.k_sb = a.k_sb; p.k_sh = a.k_sh; p.k_sl = a.k_sl;
+    p.v_sb = a.v_sb; p.v_sh = a.v_sh; p.v_sl = a.v_sl;
+    p.o_sb = a.o_sb; p.o_sh = a.o_sh; p.o_sl = a.o_sl;
+    p.mask = nullptr;
+    p.m_sb = p.m_sh = 0;
+    p.m_sl = 0;
+    p.mask_vec = 0;
+    const long long items = (long long)p.num_qb * a.B * a.H;
+    if (items <= 0 || items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    p.num_items = (int)items;
+    // one workgroup per CU; causal long/short pairs once the items
+    // outnumber the CUs
+    const long long slots = a.num_cus > 0 ? a.num_cus : 256;
+    p.upi = (CAUSAL && items > slots) ? 2 : 1;
+    p.num_units = (int)((items + p.upi - 1) / p.upi);
+    hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, LENS>), dim3((unsigned)p.num_units), dim3(512), 0,
                        stream, p);
     return hipGetLastError();
 }
@@ -367,6 +448,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16_pp(const FwdArgs& a, const Bf16Tile& t, hipStream_t s) {
+    if (t.d != a.d || a.dv != a.d || a.mask != nullptr) return hipErrorInvalidValue;
     if (t.d == 128) return launch_d<128>(a, s);
     if (t.d == 64) return launch_d<64>(a, s);
     return hipErrorInvalidValue;
