@@ -257,15 +257,26 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BParams p) {
             }
             // dS^T = P^T o (dP^T - D): accumulator r of lane (n, h) is key
             // kbase + 16(r/8) + 8h + r%8 of query row n
+            // weights; the masks (rows past Lq, keys past the key length,
+            // the causal diagonal) run as one block, only on sub-tiles that
+            // cross a boundary (a masked weight is replaced, never used, so
+            // the infinite exponential of a row without keys does no harm)
+            const bool full = q0w + 32 <= p.Lq && kbase + 32 <= kv_len && (!CAUSAL || kbase + 31 <= q0w);
+            float pv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -lse2));
+            if (!full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kbase + 16 * (r >> 3) + 8 * h + (r & 7);
+                    bool ok = row_ok && key < kv_len;
+                    if (CAUSAL) ok = ok && key <= qrow;
+                    pv[r] = ok ? pv[r] : 0.f;
+                }
+            }
             bf16x8 pb[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kbase + 16 * (r >> 3) + 8 * h + (r & 7);
-                bool ok = row_ok && key < kv_len;
-                if (CAUSAL) ok = ok && key <= qrow;
-                const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -lse2)) : 0.f;
-                pb[r >> 3][r & 7] = (__bf16)(pv * (dp[r] - dl));
-            }
+            for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)(pv[r] * (dp[r] - dl));
             // dQ^T += K^T dS^T
 #pragma unroll
             for (int st = 0; st < 2; ++st)
@@ -451,19 +462,25 @@ __global__ void __launch_bounds__(256, MODE == 0 ? 1 : 2) bwd_dkdv_kernel(BParam
             }
             // every (row, key) pair of the sub-tile valid: no masking
             const bool full = qbase + 32 <= p.Lq && k0w + 32 <= kv_len && (!CAUSAL || qbase >= k0w + 31);
+            // the masks run as one block after the exponentials, only on
+            // sub-tiles that cross a boundary
+            float pv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -lsv[r]));
+            if (!full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qrow = qbase + 16 * (r >> 3) + 8 * h + (r & 7);
+                    bool ok = key_ok && qrow < p.Lq;
+                    if (CAUSAL) ok = ok && key <= qrow;
+                    pv[r] = ok ? pv[r] : 0.f;
+                }
+            }
             bf16x8 pb[2], sb[2];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int qi = 16 * (r >> 3) + 8 * h + (r & 7);
-                const int qrow = qbase + qi;
-                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -lsv[r]));
-                if (!full) {
-                    bool ok = key_ok && qrow < p.Lq;
-                    if (CAUSAL) ok = ok && key <= qrow;
-                    pv = ok ? pv : 0.f;
-                }
-                if constexpr (DO_DV) pb[r >> 3][r & 7] = (__bf16)pv;
-                if constexpr (DO_DK) sb[r >> 3][r & 7] = (__bf16)(pv * (dp[r] - dlv[r]));
+                if constexpr (DO_DV) pb[r >> 3][r & 7] = (__bf16)pv[r];
+                if constexpr (DO_DK) sb[r >> 3][r & 7] = (__bf16)(pv[r] * (dp[r] - dlv[r]));
             }
             // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
