@@ -144,3 +144,37 @@ def test_bf16_slices_of_4gib_rejected():
     assert b.sdpa_backward(h, p(q), p(kv), p(kv), p(out), p(dout), p(lse), p(delta), p(dq), p(dk),
                            p(dv), 1, 1, Lq, Lk, d, 0, None, None) == b.NOT_SUPPORTED
     torch.cuda.synchronize()
+
+
+def test_missing_library_fails_loudly():
+    """With the HIP library absent the binding raises; there is no fallback."""
+    import subprocess
+    import sys
+    code = ("import transformer_scaled_dot_sdpa_amd.binding as b\n"
+            "try:\n"
+            "    b.load_library()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('loaded')\n")
+    env = dict(os.environ, SDPA_MI355X_LIB="/nonexistent/libsdpa_mi355x.so")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert "raised:" in out.stdout and "not found" in out.stdout, out.stdout
+
+
+def test_product_package_does_not_import_the_oracle():
+    """The oracle is test infrastructure: importing the package (and its
+    binding) must not pull it in."""
+    import subprocess
+    import sys
+    code = ("import sys\n"
+            "import transformer_scaled_dot_sdpa_amd, transformer_scaled_dot_sdpa_amd.binding\n"
+            "print(sorted(m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "[]", out.stdout
