@@ -18,9 +18,10 @@ from transformer_scaled_dot_sdpa_amd import inputs
 pytestmark = pytest.mark.gpu
 
 ALT_TILES = {
-    128: ["bf16_d128_bc64_w8", "bf16_d128_pipe_w4", "bf16_d128_pp_w8", "bf16_d128_wide_w4"],
+    128: ["bf16_d128_bc64_w8", "bf16_d128_pipe_w4", "bf16_d128_pp_w8", "bf16_d128_wide_w4",
+          "bf16_d128_mix_w8"],
     64: ["bf16_d64_bc64_w8", "bf16_d64_bc128_w4", "bf16_d64_pipe_w4", "bf16_d64_pp_w8",
-         "bf16_d64_wide_w4"],
+         "bf16_d64_wide_w4", "bf16_d64_mix_w8"],
 }
 TILE_PARAMS = [(d, t) for d, ts in ALT_TILES.items() for t in ts]
 

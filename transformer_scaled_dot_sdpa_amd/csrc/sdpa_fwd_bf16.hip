@@ -499,6 +499,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s) {
     if (t.kind == 1) return launch_fwd_bf16_pipe(a, t, s);
     if (t.kind == 2) return launch_fwd_bf16_pp(a, t, s);
     if (t.kind == 3) return launch_fwd_bf16_wide(a, t, s);
+    if (t.kind == 4) return launch_fwd_bf16_mix(a, t, s);
     if (t.d != a.d) return hipErrorInvalidValue;
     if (t.bc == 64 && t.waves == 4) {
         if (a.d == 128 && a.dv == 128) return launch_default<128, 128>(a, s);

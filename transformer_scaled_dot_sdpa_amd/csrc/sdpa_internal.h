@@ -96,7 +96,7 @@ struct Bf16Tile {
     int bc;
     int waves;
     int kind;   // 0: sdpa_fwd_bf16.hip, 1: sdpa_fwd_bf16_pipe.hip, 2: sdpa_fwd_bf16_pp.hip,
-                // 3: sdpa_fwd_bf16_wide.hip
+                // 3: sdpa_fwd_bf16_wide.hip, 4: sdpa_fwd_bf16_mix.hip
     const char* name;
 };
 
@@ -110,6 +110,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_bf16_pipe(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_bf16_pp(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_bf16_wide(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
+hipError_t launch_fwd_bf16_mix(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s);

@@ -21,12 +21,14 @@ const Bf16Tile kTiles[] = {
     {128, 64, 8, 2, "bf16_d128_pp_w8"},
     {128, 64, 8, 0, "bf16_d128_bc64_w8"},
     {128, 64, 4, 3, "bf16_d128_wide_w4"},
+    {128, 64, 8, 4, "bf16_d128_mix_w8"},
     {64, 64, 4, 0, "bf16_d64_bc64_w4"},
     {64, 64, 4, 1, "bf16_d64_pipe_w4"},
     {64, 64, 8, 2, "bf16_d64_pp_w8"},
     {64, 128, 4, 0, "bf16_d64_bc128_w4"},
     {64, 64, 8, 0, "bf16_d64_bc64_w8"},
     {64, 64, 4, 3, "bf16_d64_wide_w4"},
+    {64, 64, 8, 4, "bf16_d64_mix_w8"},
 };
 }  // namespace
 
