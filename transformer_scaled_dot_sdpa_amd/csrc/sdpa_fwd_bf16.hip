@@ -266,15 +266,13 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
 #pragma unroll
                 for (int u = i * KCH / NM; u < (i + 1) * KCH / NM; ++u) load_k(lt, lb, u);
             }
-        }
-
-        // additive mask, in raw-score units (the weights take s * sl)
-        if constexpr (MASK) {
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
+            // additive mask, in raw-score units (the weights take s * sl);
+            // added per sub-tile, so that its registers free up early
+            if constexpr (MASK) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     s[kt][r] = __builtin_fmaf(mb[kt][r >> 2][r & 3], p.inv_scale, s[kt][r]);
+            }
         }
         // masks: padding / ragged tail and the causal diagonal
         const bool need_mask = (ts + BC > kv_len) || (CAUSAL && ts + BC - 1 > q0w);
