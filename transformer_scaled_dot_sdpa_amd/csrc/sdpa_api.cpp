@@ -240,6 +240,7 @@ sdpa_status_t sdpa_backward(sdpa_handle_t h, const void* q, const void* k, const
     a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.delta = delta;
     a.dq = dq; a.dk = dk; a.dv = dv; a.key_lens = key_lens;
     a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk; a.d = d_k; a.causal = causal;
+    a.num_cus = h->num_cus;
 
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) {

@@ -12,10 +12,11 @@
 // P is recomputed from S and the forward's log-sum-exp (P = exp(S - lse)),
 // so no score matrix is stored.
 //
-// Three kernels:
-//   bwd_delta   D = rowsum(dO o O), one value per query row (fp32);
-//   bwd_dq      per block of 128 query rows (32 per wavefront): stream K and
-//               V tiles of 64 keys through LDS and accumulate
+// Two kernels:
+//   bwd_dq      per block of 128 query rows (32 per wavefront): first
+//               D = rowsum(dO o O) of the wavefront's rows (fp32, also
+//               written out for the next kernel), then stream K and V tiles
+//               of 64 keys through LDS and accumulate
 //               dQ^T += K^T dS^T  after  S^T = K Q^T, dP^T = V dO^T;
 //   bwd_dkdv    per block of 128 keys (32 per wavefront): stream Q and dO
 //               tiles of 64 query rows through LDS and accumulate
@@ -67,32 +68,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // is faster)
 template <int D>
 constexpr bool kSplitDkDv = D == 128;
-
-// ---------------------------------------------------------------- D
-template <int D>
-__global__ void __launch_bounds__(256) bwd_delta_kernel(const uint16_t* __restrict__ o,
-                                                        const uint16_t* __restrict__ dout,
-                                                        float* __restrict__ delta, long long rows) {
-    constexpr int CH = D / 8;                  // 16-byte chunks per row (lanes per row)
-    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long row = gid / CH;
-    const int c = (int)(gid % CH);
-    float acc = 0.f;
-    if (row < rows) {
-        // a bf16 value widens to fp32 by placing its bits in the high half
-        const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + c * 8);
-        const uint4 g = *reinterpret_cast<const uint4*>(dout + row * D + c * 8);
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, gw[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc = fmaf(__uint_as_float(aw[e] << 16), __uint_as_float(gw[e] << 16), acc);
-            acc = fmaf(__uint_as_float(aw[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), acc);
-        }
-    }
-#pragma unroll
-    for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (row < rows && c == 0) delta[row] = acc;
-}
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row of a backward
 // tile.  Tiles here are read both ways: ds_read_b128 of one chunk from 16
@@ -222,8 +197,29 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BParams p) {
         }
     }
     const float lse2 = p.lse[(size_t)bh * p.Lq + qr] * kLog2e;
-    const float dl = p.delta[(size_t)bh * p.Lq + qr];
     const bool row_ok = qrow < p.Lq;
+    // D = dO . O of the row, in fp32: this lane holds half of the row's dO
+    // (the B-operand chunks) and reads the matching half of O; a bf16 value
+    // widens to fp32 by placing its bits in the high half.  Written out for
+    // the dK/dV kernels, which run after this one.
+    float dl;
+    {
+        const uint4* so = reinterpret_cast<const uint4*>(p.o + q_base + (size_t)qr * D + 8 * h);
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const uint4 a = so[2 * ks];
+            const uint4 g = __builtin_bit_cast(uint4, df[ks]);
+            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                part = fmaf(__uint_as_float(aw[e] << 16), __uint_as_float(gw[e] << 16), part);
+                part = fmaf(__uint_as_float(aw[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), part);
+            }
+        }
+        dl = sum_across_halves(part);
+        if (row_ok && h == 0) p.delta[(size_t)bh * p.Lq + qrow] = dl;
+    }
 
     auto issue_loads = [&](int t, uint16_t* kb, uint16_t* vb) __attribute__((always_inline)) {
         const uint32_t toff = (uint32_t)(t * BC) * D * 2;
@@ -569,22 +565,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.scale = (float)(1.0 / sqrt((double)D));
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
 
-    const long long rows = (long long)a.B * a.H * a.Lq;
-    {
-        const long long threads = rows * (D / 8);
-        const long long blocks = (threads + 255) / 256;
-        if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           p.o, p.dout, p.delta, rows);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    // causal work runs as long/short pairs of items once the items
+    // outnumber the resident workgroups (2 per CU); a smaller problem takes
+    // one item per workgroup so that every item starts at once
+    const long long slots = (long long)(a.num_cus > 0 ? a.num_cus : 256) * 2;
     {
         p.num_blocks = (a.Lq + 127) / 128;
         const long long items = (long long)p.num_blocks * a.B * a.H;
         if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         p.num_items = (int)items;
-        p.upi = CAUSAL ? 2 : 1;
+        p.upi = (CAUSAL && items > slots) ? 2 : 1;
         p.num_units = (int)((items + p.upi - 1) / p.upi);
         hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, LENS>), dim3((unsigned)p.num_units), dim3(256), 0,
                            stream, p);
@@ -596,7 +586,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         const long long items = (long long)p.num_blocks * a.B * a.H;
         if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         p.num_items = (int)items;
-        p.upi = CAUSAL ? 2 : 1;
+        p.upi = (CAUSAL && items > slots) ? 2 : 1;
         p.num_units = (int)((items + p.upi - 1) / p.upi);
         if constexpr (kSplitDkDv<D>) {
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, LENS, 1>), dim3((unsigned)p.num_units), dim3(256), 0,

@@ -62,6 +62,7 @@ struct BwdArgs {
     const int32_t* key_lens;
     int B, H, Lq, Lk, d;
     int causal;
+    int num_cus;              // compute units of the device (sizes the work units)
 };
 
 // Arguments of the decode-shaped forward: FwdArgs plus the caller's
