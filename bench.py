@@ -224,7 +224,7 @@ def backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args, fwd_flops_alg)
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                          "algorithmic_flops_per_call": flops,
-                         "kernels": "bwd_delta_kernel, bwd_dq_kernel, bwd_dkdv_kernel"}}
+                         "kernels": "bwd_dq_kernel (with D), bwd_dkdv_kernel"}}
     if cpu is not None:
         out["cpu_baseline"] = cpu
     return out
