@@ -387,13 +387,22 @@ __global__ void __launch_bounds__(256, MODE == 0 ? 1 : 2) bwd_dkdv_kernel(BParam
     }
     const bool key_ok = key < kv_len;
 
-    // per-row statistics of a query tile (lse in exp2 units and D), loaded
-    // by the first 128 threads into registers, stored to LDS before the
-    // barrier that opens the tile.  The load is consumed only at the store:
-    // any arithmetic on it right after the load would make the wavefront
-    // wait for all its loads in flight, the next tile's included.
+    // per-row statistics of a query tile, loaded by the first 128 threads
+    // into registers and stored to LDS before the barrier that opens the
+    // tile: the lse and D.  With dK (S_START) the lse is stored as
+    // -lse / scale (raw score units) and is the starting value of the S
+    // product, so that the accumulator over the scale is the exponent of P
+    // and the registers of a separate lse vector stay free for the dK pass;
+    // the dV-only pass stores lse in exp2 units and subtracts it, which
+    // keeps the LDS read off the path to its first product.  dP starts from
+    // zero and D is subtracted afterwards: with one valid key dP and D are
+    // then the same fp32 dot product and dS is exactly zero.  The load is
+    // consumed only at the store: any arithmetic on it right after the load
+    // would make the wavefront wait for all its loads in flight, the next
+    // tile's included.
+    constexpr bool S_START = DO_DK;
     float stat = 0.f;
-    const float stat_mul = tid < BQ ? kLog2e : 1.f;
+    const float stat_mul = tid < BQ ? (S_START ? -1.f / p.scale : kLog2e) : 1.f;
     auto stat_load = [&](int t) __attribute__((always_inline)) {
         if (tid < 2 * BQ) {
             int row = t * BQ + (tid & (BQ - 1));
@@ -426,9 +435,32 @@ __global__ void __launch_bounds__(256, MODE == 0 ? 1 : 2) bwd_dkdv_kernel(BParam
             // causal: rows of this sub-tile all before the wavefront's first key
             if (CAUSAL && qbase + 31 < k0w) continue;
             if (qbase >= p.Lq) continue;
+            // accumulator r of lane (n, h) is query row qbase + 16(r/8) + 8h +
+            // r%8 against key `key`; the row statistics of rows 16j + 8h +
+            // 0..7 are read as vectors
             f32x16 s, dp;
+            float lsv[16];
+            auto read_lse = [&](float* dst) __attribute__((always_inline)) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+                for (int j = 0; j < 2; ++j) {
+                    const float4* s0 = reinterpret_cast<const float4*>(&st_lds[buf][0][32 * qt + 16 * j + 8 * h]);
+                    const float4 u0 = s0[0], u1 = s0[1];
+                    const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dst[8 * j + e] = uu[e];
+                }
+            };
+            if constexpr (S_START) {
+                float st[16];
+                read_lse(st);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] = st[r];
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if constexpr (!S_START) s[r] = 0.f;
+                dp[r] = 0.f;
+            }
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + qt * 32 * D + off.rd[ks]);
@@ -438,22 +470,19 @@ __global__ void __launch_bounds__(256, MODE == 0 ? 1 : 2) bwd_dkdv_kernel(BParam
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
                 }
             }
-            // accumulator r of lane (n, h) is query row qbase + 16(r/8) + 8h +
-            // r%8 against key `key`
-            // the row statistics of rows 16j + 8h + 0..7, read as vectors
-            // before any use so that no load sits under a mask
-            float lsv[16], dlv[16];
+            // (the dV-only pass reads the lse here, after its products)
+            if constexpr (!S_START) read_lse(lsv);
+            // D of the same rows, read as vectors before any use so that no
+            // load sits under a mask
+            float dlv[16];
+            if constexpr (DO_DK) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float4* s0 = reinterpret_cast<const float4*>(&st_lds[buf][0][32 * qt + 16 * j + 8 * h]);
-                const float4* s1 = reinterpret_cast<const float4*>(&st_lds[buf][1][32 * qt + 16 * j + 8 * h]);
-                const float4 u0 = s0[0], u1 = s0[1], w0 = s1[0], w1 = s1[1];
-                const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-                const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                for (int j = 0; j < 2; ++j) {
+                    const float4* s1 = reinterpret_cast<const float4*>(&st_lds[buf][1][32 * qt + 16 * j + 8 * h]);
+                    const float4 w0 = s1[0], w1 = s1[1];
+                    const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    lsv[8 * j + e] = uu[e];
-                    dlv[8 * j + e] = ww[e];
+                    for (int e = 0; e < 8; ++e) dlv[8 * j + e] = ww[e];
                 }
             }
             // every (row, key) pair of the sub-tile valid: no masking
@@ -462,7 +491,9 @@ __global__ void __launch_bounds__(256, MODE == 0 ? 1 : 2) bwd_dkdv_kernel(BParam
             // sub-tiles that cross a boundary
             float pv[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -lsv[r]));
+            for (int r = 0; r < 16; ++r)
+                pv[r] = __builtin_amdgcn_exp2f(S_START ? s[r] * p.scale_log2
+                                                       : __builtin_fmaf(s[r], p.scale_log2, -lsv[r]));
             if (!full) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
