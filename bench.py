@@ -108,6 +108,21 @@ def read_traffic(workload: str):
     return float(m_val.group(1))
 
 
+def host_cpu():
+    """Model name and thread counts of the host the oracle runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(w, q, k, v, key_lens, out_gpu, lse_gpu, target_s: float):
     """Time the CPU oracle on whole (b, h) slices of the workload."""
     import numpy as np
@@ -130,6 +145,17 @@ def cpu_baseline(w, q, k, v, key_lens, out_gpu, lse_gpu, target_s: float):
         if nheads > 1:
             t1, rows, o, l = run(nheads)
     value = nheads * per_head_flops / t1 / 1e12
+    # the same oracle on one thread, over the first rows of slice 0 up to
+    # about 2 million (query, key) pairs, with the flops of exactly those rows
+    kl0 = w.Lk if key_lens is None else max(0, min(w.Lk, int(key_lens[0])))
+    all_rows = np.arange(w.Lq, dtype=np.int64)
+    valid = np.minimum(kl0, all_rows + 1) if w.causal else np.full(w.Lq, kl0)
+    n1 = int(max(1, np.searchsorted(np.cumsum(valid), 2_000_000, side="right")))
+    rows1 = all_rows[:n1]
+    flops1 = 4.0 * w.d * float(valid[:n1].sum())
+    t0 = time.perf_counter()
+    oracle.sdpa_rows(q, k, v, rows1, causal=w.causal, key_lens=key_lens, bf16=bf16, nthreads=1)
+    t_one = time.perf_counter() - t0
     og = out_gpu.reshape(-1, w.d)[rows]
     lg = lse_gpu.reshape(-1)[rows]
     fin = np.isfinite(l)
@@ -142,6 +168,9 @@ def cpu_baseline(w, q, k, v, key_lens, out_gpu, lse_gpu, target_s: float):
                    f"{nheads * per_head_flops / 1e9:.2f} GFLOP headline), fp64, "
                    f"{t1:.2f} s wall"),
         "seconds": t1,
+        "host": host_cpu(),
+        "one_thread": {"value": flops1 / t_one / 1e12, "unit": "TFLOP/s (algorithmic)",
+                       "sample": f"query rows 0..{n1 - 1} of slice 0, {t_one:.2f} s wall"},
         "sample_max_abs_out_vs_gpu": float(np.max(np.abs(og - o))),
         "sample_max_abs_lse_vs_gpu": float(np.max(np.abs(lg[fin] - l[fin]), initial=0.0)),
     }
