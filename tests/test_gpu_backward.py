@@ -9,7 +9,14 @@ max |g - r| <= 2e-2 * max |r| and ||g - r||_2 <= 1e-2 * ||r||_2 -- the
 forward's bf16 bar stated relative to the tensor's scale, since gradients
 are not of order 1; for fp32, max |g - r| <= 1e-5 * max(1, max |r|).
 Gradients that the masks make exactly zero (keys no row sees, rows with no
-key) must be exactly zero.
+key) must be exactly zero.  A reference that is zero everywhere for another
+reason -- every row with a single valid key, where the softmax Jacobian's
+rows sum to zero and dS = P (dP - D) cancels -- makes the relative bar
+degenerate: on the GPU dP and D are two fp32 dot products of d terms, summed
+in different orders, so their difference is a rounding residue.  There the
+bar is the standard error bound of such a difference, 2 d u sum_t |dO_t O_t|
+(u = 2^-24), times the largest |q| or |k| and the scale, with a factor 4 of
+room.
 """
 import numpy as np
 import pytest
@@ -49,14 +56,26 @@ def oracle_grads(q, k, v, dout, dtype, causal=False, key_lens=None):
     return oracle.sdpa_bwd(q, k, v, dout, causal=causal, key_lens=key_lens, bf16=(dtype == "bf16"))
 
 
-def assert_grad_close(g, r, dtype, what):
+def cancellation_floor(q, k, dout, out, dtype):
+    """Bound on |dQ|, |dK| where dS cancels exactly in real arithmetic: the
+    fp32 error of dP - D (two d-term dot products), 2 d u sum_t |dO_t O_t|,
+    times max(|q|, |k|) and 1/sqrt(d), with a factor 4 of room."""
+    d = q.shape[-1]
+    g64 = inputs.as_float(dout, dtype).astype(np.float64)
+    row = np.abs(g64 * out.astype(np.float64)).sum(-1).max(initial=0.0)
+    qk = max(np.abs(inputs.as_float(q, dtype)).max(initial=0.0), np.abs(inputs.as_float(k, dtype)).max(initial=0.0))
+    return 4.0 * 2.0 * d * 2.0 ** -24 * row * float(qk) / np.sqrt(d)
+
+
+def assert_grad_close(g, r, dtype, what, zero_floor=0.0):
     assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
     g = g.astype(np.float64)
     err = np.abs(g - r)
     scale = float(np.max(np.abs(r))) if r.size else 0.0
     if dtype == "bf16":
         if scale == 0.0:
-            assert np.all(g == 0), f"{what}: expected all zeros"
+            assert err.max(initial=0.0) <= zero_floor, \
+                f"{what}: reference all zero, max |g| = {err.max(initial=0.0):.3g} > {zero_floor:.3g}"
             return
         assert err.max() <= BF16_MAX_REL * scale, \
             f"{what}: max |d| = {err.max():.3g} > {BF16_MAX_REL} * {scale:.3g}"
@@ -86,8 +105,9 @@ def check_case(B, H, Lq, Lk, d, dtype, causal, kl, seed, what):
     dout = inputs.generate_dout(B, H, Lq, d, dtype, seed)
     dq, dk, dv, delta, out = run_fwd_bwd(q, k, v, dout, dtype, causal, kl)
     rq, rk, rv = oracle_grads(q, k, v, dout, dtype, causal, kl)
+    floor = cancellation_floor(q, k, dout, out, dtype)
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        assert_grad_close(g, r, dtype, f"{what} {name}")
+        assert_grad_close(g, r, dtype, f"{what} {name}", zero_floor=floor)
     assert_structural_zeros(dq, dk, dv, Lq, Lk, causal, kl, what)
     # delta is documented as dout . out per row, in fp32
     g64 = inputs.as_float(dout, dtype).astype(np.float64)
