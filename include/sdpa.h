@@ -201,6 +201,10 @@ sdpa_status_t sdpa_forward_ex(sdpa_handle_t h, const sdpa_forward_desc_t* desc, 
  * Accumulation is fp32 on every path.  bf16: the five products on bf16
  * matrix cores, the recomputed weights and dL/ds rounded to bf16 (RNE) as
  * operands; results rounded to bf16 (RNE).  Deterministic: no atomics.
+ * dout . v_j and D are two fp32 dot products summed in different orders, so
+ * where dL/ds cancels exactly in real arithmetic (a row with one valid key)
+ * dq and dk hold a rounding residue of order 2^-24 d_k |dout| |v| rather
+ * than an exact zero.
  *
  * Errors (returned before anything is enqueued; outputs untouched):
  * INVALID_VALUE for a NULL handle or pointer (key_lens aside), sizes < 1,
