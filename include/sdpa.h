@@ -235,8 +235,11 @@ sdpa_status_t sdpa_backward(sdpa_handle_t h,
  * the GPU; each chunk yields a partial output and log-sum-exp, merged as
  * lse = ln sum_c e^{lse_c}, out = sum_c e^{lse_c - lse} out_c (the ratio
  * identity of the formula page "トランスフォーマーの注意機構", section 証明,
- * with the log-sum-exp of section 広がる学問).  The partial results live in
- * a caller-owned workspace:
+ * with the log-sum-exp of section 広がる学問).  With at least two slices per
+ * compute unit (and d_k = 64, or at most 4096 keys) the slices already fill
+ * the GPU: the call then runs sdpa_forward's kernel, one workgroup per
+ * slice, with no split and no workspace.  The partial results of a split
+ * live in a caller-owned workspace:
  *   workspace        device memory of at least workspace_bytes, 4-byte
  *                    aligned, not overlapping any other argument; contents
  *                    on entry are ignored and on return unspecified.  May be

@@ -46,7 +46,7 @@ CASES = [
     (2, 1, 4, 640, False, [-5, 10000]),
     (1, 2, 5, 300, True, None),
     (2, 3, 1, 2050, False, [2049, 1]),
-    (64, 32, 1, 256, False, None),      # many slices: one chunk each
+    (64, 32, 1, 256, False, None),      # many slices: the forward kernel
 ]
 
 
@@ -74,7 +74,13 @@ def test_decode_split_and_single_chunk_both_exercised():
     assert sdpa.decode_workspace_size(q, k) > 0          # few slices: split over keys
     q = torch.empty((64, 32, 1, 128), dtype=torch.bfloat16, device="cuda")
     k = torch.empty((64, 32, 256, 128), dtype=torch.bfloat16, device="cuda")
-    assert sdpa.decode_workspace_size(q, k) == 0         # many slices: one chunk each
+    assert sdpa.decode_workspace_size(q, k) == 0         # many slices: the forward kernel
+    q = torch.empty((2, 1, 1, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((2, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
+    assert sdpa.decode_workspace_size(q, k) == 0         # short keys: one chunk of the decode kernel
+    q = torch.empty((16, 32, 1, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((16, 32, 8192, 128), dtype=torch.bfloat16, device="cuda")
+    assert sdpa.decode_workspace_size(q, k) > 0          # d = 128, 8192 keys: split kernel
 
 
 @pytest.mark.parametrize("name", ["decode_d128", "decode_d64_single"])

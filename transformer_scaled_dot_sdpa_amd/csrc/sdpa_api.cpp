@@ -409,6 +409,7 @@ sdpa_status_t sdpa_decode(sdpa_handle_t h, const void* q, const void* k, const v
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.key_lens = key_lens;
     a.workspace = workspace;
     a.B = B; a.H = H; a.Lq = Lq; a.Lk = Lk; a.d = d_k; a.causal = causal;
+    a.num_cus = h->num_cus;
 
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) {

@@ -331,6 +331,22 @@ hipError_t launch_d(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s) 
 
 DecodePlan plan_decode(int B, int H, int Lq, int Lk, int d, int num_cus) {
     DecodePlan plan;
+    // With at least two slices per compute unit the main forward kernel,
+    // one workgroup streaming a whole slice's K and V through LDS, moves the
+    // bytes faster than the split kernel below (measured on MI355X, Lq = 1,
+    // warmed clocks: 3-5% at d = 128 with 512-1536 slices of 2048 keys, 5-16%
+    // at d = 64), except for d = 128 beyond 4096 keys, where the split
+    // kernel stays about 3% ahead.
+    const long long n_slices = (long long)B * H;
+    const int cus = num_cus > 0 ? num_cus : 256;
+    plan.use_forward = n_slices >= 2LL * cus && (d == 64 || Lk <= 4096) &&
+                       (long long)Lk * d * 2 < (1LL << 32);
+    if (plan.use_forward) {
+        plan.splits = 1;
+        plan.chunk = Lk;
+        plan.workspace_bytes = 0;
+        return plan;
+    }
     // step of the kernel: 4 wavefronts x 64/(d/8) rows; chunks of about
     // 256 KiB of keys and values, and at least 4 workgroups per compute
     // unit, so that chunks of uneven length (key_lens) still balance; never
@@ -356,6 +372,15 @@ DecodePlan plan_decode(int B, int H, int Lq, int Lk, int d, int num_cus) {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s) {
     if (a.Lq < 1 || a.Lq > kDecodeMaxLq) return hipErrorInvalidValue;
+    if (plan.use_forward) {
+        FwdArgs f;
+        f.q = a.q; f.k = a.k; f.v = a.v; f.out = a.out; f.lse = a.lse; f.key_lens = a.key_lens;
+        f.B = a.B; f.H = a.H; f.Lq = a.Lq; f.Lk = a.Lk; f.d = a.d; f.causal = a.causal;
+        f.num_cus = a.num_cus;
+        f.set_contiguous();
+        const Bf16Tile tile{a.d, 64, 4, 0, nullptr};
+        return launch_fwd_bf16(f, tile, s);
+    }
     if (a.d == 128) return launch_d<128>(a, plan, s);
     if (a.d == 64) return launch_d<64>(a, plan, s);
     return hipErrorInvalidValue;

@@ -77,6 +77,7 @@ struct DecodeArgs {
     void* workspace;          // plan.workspace_bytes, 4-byte aligned (unused with one chunk)
     int B, H, Lq, Lk, d;
     int causal;
+    int num_cus;              // compute units of the device
 };
 
 // Largest number of query rows the decode kernel takes.
@@ -87,6 +88,8 @@ struct DecodePlan {
     int splits;               // key chunks per (b, h)
     int chunk;                // keys per chunk
     size_t workspace_bytes;   // 0 when splits == 1
+    bool use_forward;         // enough slices to fill the GPU: the main forward
+                              // kernel (one workgroup per slice, no workspace)
 };
 DecodePlan plan_decode(int B, int H, int Lq, int Lk, int d, int num_cus);
 
