@@ -136,6 +136,12 @@ typedef struct {
  *                decoder mask this way).  A row whose valid keys all carry
  *                -inf gets out = 0 and lse = -inf.
  * causal and key_lens apply as in sdpa_forward, on top of the mask.
+ *   tile         NULL for the configuration sdpa_forward would choose, or the
+ *                name of a compiled one ("bf16_d64_bc64_w4_ks2", ...; fp32:
+ *                "f32_wave_per_row").  Every configuration computes the same
+ *                function; they differ in speed.  d_v != d_k and a mask run
+ *                only in the default bf16 configuration of each d_k
+ *                ("bf16_d64_bc64_w4", "bf16_d128_bc64_w4").
  */
 typedef struct {
     const void* q;
@@ -150,6 +156,10 @@ typedef struct {
     float scale;
     const float* mask;
     sdpa_layout_t mask_layout;
+    const char* tile;           /* NULL: chosen by shape (see sdpa_kernel_name);
+                                   else the name of one compiled bf16 tile
+                                   configuration (sdpa_kernel_name's strings),
+                                   for tuning and tests */
 } sdpa_forward_desc_t;
 
 /*
@@ -162,9 +172,12 @@ typedef struct {
  * its strides are multiples of 4.
  * Errors (before anything is enqueued): INVALID_VALUE for desc == NULL, a
  * NULL tensor, sizes < 1, causal not 0/1, a row stride below the width, a
- * negative stride, element counts overflowing int64, or out overlapping
- * any input (by extent); NOT_SUPPORTED for the dtype limits above;
- * HIP_ERROR if the launch fails.
+ * negative stride, element counts overflowing int64, an out view in which
+ * two elements share an address (a zero stride on a dimension of size > 1,
+ * or strides whose rows interleave), or out overlapping any input (by
+ * extent); NOT_SUPPORTED for the dtype limits above, or a tile name that is
+ * not compiled for this d_k (or cannot take this d_v or mask); HIP_ERROR if
+ * the launch fails.
  */
 sdpa_status_t sdpa_forward_ex(sdpa_handle_t h, const sdpa_forward_desc_t* desc, void* stream);
 

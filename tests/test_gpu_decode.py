@@ -49,6 +49,16 @@ CASES = [
     (64, 32, 1, 256, False, None),      # many slices: the forward kernel
 ]
 
+# At least two slices per compute unit: sdpa_decode runs the main forward
+# kernel, one workgroup per slice, with no workspace.  Several query rows,
+# the causal flag and key lengths 0, 1, short, full and out of range.
+FORWARD_CASES = [
+    # B, H, Lq, Lk, causal, key_lens
+    (64, 8, 5, 300, True, None),
+    (64, 8, 8, 700, False, [0, 1, 2, 63, 64, 65, 699, 700, 701, -3] + [350] * 54),
+    (64, 8, 2, 129, True, [0, 1, 64, 128, 129, 1000] + [100] * 58),
+]
+
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}q{}k{}c{}L{}".format(*c))
@@ -60,6 +70,28 @@ def test_decode_matches_oracle(d, case):
     o, l, need = run_decode(q, k, v, causal, kl)
     ro, rl = oracle_ref(q, k, v, "bf16", causal, kl)
     assert_close(o, l, ro, rl, "bf16", f"decode {case}")
+    if kl is not None:
+        for b, n in enumerate(kl):
+            if n <= 0:
+                assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", FORWARD_CASES, ids=lambda c: "B{}H{}q{}k{}c{}".format(*c[:5]))
+def test_decode_forward_backed_matches_oracle(d, case):
+    import torch
+    import transformer_scaled_dot_sdpa_amd as sdpa
+    B, H, Lq, Lk, causal, kl = case
+    qe = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device="cuda")
+    ke = torch.empty((B, H, Lk, d), dtype=torch.bfloat16, device="cuda")
+    assert sdpa.decode_workspace_size(qe, ke) == 0      # the forward-backed path
+    seed = 1400 + d + 7 * Lq + Lk
+    announce(f"decode (forward kernel) d{d} B{B} H{H} Lq{Lq} Lk{Lk} causal={causal} seed={seed}")
+    q, k, v, _ = inputs.generate(B, H, Lq, Lk, d, "bf16", seed)
+    o, l, need = run_decode(q, k, v, causal, kl)
+    assert need == 0
+    ro, rl = oracle_ref(q, k, v, "bf16", causal, kl)
+    assert_close(o, l, ro, rl, "bf16", f"decode forward-backed {case}")
     if kl is not None:
         for b, n in enumerate(kl):
             if n <= 0:

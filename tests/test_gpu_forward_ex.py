@@ -137,6 +137,38 @@ def test_ex_masks(dtype, dk):
     assert_close(o, l, ro, rl, dtype, "mask + causal + key_lens")
 
 
+@pytest.mark.parametrize("dtype,dk", [("bf16", 64), ("bf16", 128), ("fp32", 8)])
+def test_ex_left_padded_mask(dtype, dk):
+    """A mask that drops each row's first keys (left padding): for many
+    rows the whole first key tile, or the first two, are -inf, and the row's
+    reference maximum must come from the first tile with a finite score.  The
+    result equals attention over the remaining keys alone."""
+    B, H, Lq, Lk = 2, 2, 200, 330
+    seed = 3300 + dk
+    q = draw(B, H, Lq, dk, dtype, seed)
+    k = draw(B, H, Lk, dk, dtype, seed + 1)
+    v = draw(B, H, Lk, dk, dtype, seed + 2)
+    start = np.array([[70, 130], [0, 200]])   # first valid key per (batch, row half)
+    m = np.zeros((B, 1, Lq, Lk), np.float32)
+    for b in range(B):
+        for half in range(2):
+            m[b, 0, half * Lq // 2:(half + 1) * Lq // 2, :start[b, half]] = -np.inf
+    rng = np.random.default_rng(seed)
+    m += np.where(np.isinf(m), 0.0, rng.standard_normal(m.shape) * 0.5).astype(np.float32)
+    announce(f"forward_ex left-padded mask {dtype} d{dk}")
+    o, l = run_ex(q, k, v, dtype, mask=m)
+    ro, rl = oracle_ex(q, k, v, dtype, mask=m)
+    assert_close(o, l, ro, rl, dtype, "left-padded mask")
+    # the same rows with the dropped keys cut away: the plain definition
+    for b in range(B):
+        for half in range(2):
+            rows = slice(half * Lq // 2, (half + 1) * Lq // 2)
+            s0 = int(start[b, half])
+            rc, lc = oracle_ex(q[b:b + 1, :, rows], k[b:b + 1, :, s0:], v[b:b + 1, :, s0:], dtype,
+                               mask=m[b:b + 1, :, rows, s0:])
+            assert_close(o[b:b + 1, :, rows], l[b:b + 1, :, rows], rc, lc, dtype, f"cut b{b} half{half}")
+
+
 def test_ex_packed_qkv_and_contiguous_identity():
     """q, k, v read out of one packed [B, L, 3, H, d] buffer; and on
     contiguous tensors with default arguments forward_ex is the forward,
@@ -213,6 +245,14 @@ def test_ex_validation():
     assert b.sdpa_forward_ex(h, desc(out=x.data_ptr()), None) == b.INVALID_VALUE       # out aliases q
     assert b.sdpa_forward_ex(h, desc(q_layout=b.Layout(0, 0, 64)), None) == b.INVALID_VALUE  # row < d_k
     assert b.sdpa_forward_ex(h, desc(q_layout=b.Layout(-8, 0, 128)), None) == b.INVALID_VALUE
+    # out views whose elements alias: a zero batch or head stride over a
+    # dimension of size 2, heads interleaved inside a row, rows inside a head
+    for lay in (b.Layout(0, 64 * 128, 128), b.Layout(2 * 64 * 128, 0, 128), b.Layout(2 * 64 * 256, 64, 256),
+                b.Layout(2 * 64 * 128, 32 * 128, 128), b.Layout(64 * 128, 64 * 128, 128)):
+        assert b.sdpa_forward_ex(h, desc(out_layout=lay), None) == b.INVALID_VALUE, (lay.batch, lay.head, lay.row)
+    # the same buffer as a head-interleaved view is one-to-one and accepted
+    assert b.sdpa_forward_ex(h, desc(out_layout=b.Layout(64 * 256, 128, 256)), None) == b.SUCCESS
+    torch.cuda.synchronize()
     assert b.sdpa_forward_ex(h, desc(d_v=96), None) == b.NOT_SUPPORTED
     assert b.sdpa_forward_ex(h, desc(k_layout=b.Layout(8448, 4224, 132)), None) == b.NOT_SUPPORTED
     m = torch.zeros(64, 64, device="cuda")

@@ -63,6 +63,27 @@ def test_large_workload_sampled_rows(large_run):
     assert rel < 1e-2, rel
 
 
+def test_large_workload_whole_slices(large_run):
+    """Sixteen whole (b, h) slices (4096 rows each) against the oracle.  The
+    slices are spread over the work schedule: units of long/short item pairs
+    are handed to the 8 XCDs in contiguous ranges of 48 slices, and two
+    slices are taken from each range (one near its start, one near its
+    end), so every XCD's share and both ends of a range are checked."""
+    import oracle
+    w, q, k, v, o, l = large_run
+    per_xcd = w.B * w.H // 8
+    slices = [x * per_xcd + off for x in range(8) for off in (3, per_xcd - 5)]
+    assert len(set(slices)) == 16 and max(slices) < w.B * w.H
+    rows = np.concatenate([np.arange(bh * w.Lq, (bh + 1) * w.Lq, dtype=np.int64) for bh in slices])
+    announce(f"large_causal_d128: oracle on whole slices {slices}")
+    ro, rl = oracle.sdpa_rows(q, k, v, rows, causal=True, bf16=True)
+    og = o.reshape(-1, w.d)[rows]
+    lg = l.reshape(-1)[rows]
+    assert_close(og, lg, ro, rl, "bf16", f"large_causal_d128 whole slices {slices}")
+    rel = np.linalg.norm(og - ro) / np.linalg.norm(ro)
+    assert rel < 1e-2, rel
+
+
 def test_large_workload_row0_is_v0(large_run):
     """Causal row 0 attends only key 0 with weight exactly 1: O = V[0] bitwise."""
     w, q, k, v, o, l = large_run

@@ -1,29 +1,27 @@
-"""Every bf16 tile configuration the library ships, not only the default one,
-against the CPU oracle through the C ABI.
+"""Every bf16 tile configuration the library compiles, not only the ones the
+selector picks for the workloads, against the CPU oracle through the C ABI.
 
-The tile is chosen by name with the SDPA_FORCE_TILE environment variable,
-which the library reads on every call.  The cases cover several key tiles, a
-ragged tail, key lengths (empty, short, full), causal with Lq > Lk and
+A tile is forced by name through ``sdpa_forward_ex``'s ``tile`` field.  The
+cases cover one key tile and many (odd and even counts, so that one group of
+a key-split tile can have nothing to do in the last step, or in every step),
+ragged tails, key lengths (empty, short, full, tied; odd item counts for the
+tiles that pair items by key length), causal with Lq > Lk and
 Lq < Lk, query blocks that end inside a tile, and scores that grow along the
 keys far enough to make the kernels redo a workgroup with a running maximum.
 """
-import os
-
 import numpy as np
 import pytest
 
-from gpu_util import announce, assert_close, generate, oracle_ref, require_gpu, run_gpu
+from gpu_util import announce, assert_close, generate, oracle_ref, require_gpu, to_device
 from transformer_scaled_dot_sdpa_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-ALT_TILES = {
-    128: ["bf16_d128_bc64_w8", "bf16_d128_pipe_w4", "bf16_d128_pp_w8", "bf16_d128_wide_w4",
-          "bf16_d128_mix_w8"],
-    64: ["bf16_d64_bc64_w8", "bf16_d64_bc128_w4", "bf16_d64_pipe_w4", "bf16_d64_pp_w8",
-         "bf16_d64_wide_w4", "bf16_d64_mix_w8"],
+TILES = {
+    128: ["bf16_d128_bc64_w4", "bf16_d128_bc64_w4_pairs", "bf16_d128_bc64_w4_ks2", "bf16_d128_bc64_w8"],
+    64: ["bf16_d64_bc64_w4", "bf16_d64_bc64_w4_pairs", "bf16_d64_bc64_w8"],
 }
-TILE_PARAMS = [(d, t) for d, ts in ALT_TILES.items() for t in ts]
+TILE_PARAMS = [(d, t) for d, ts in TILES.items() for t in ts]
 
 CASES = [
     # B, H, Lq, Lk, causal, key_lens
@@ -34,53 +32,49 @@ CASES = [
     (1, 2, 300, 130, True, None),
     (1, 2, 100, 333, True, None),
     (2, 1, 520, 520, True, [300, 520]),
+    (2, 2, 256, 512, False, [64, 450]),
+    (4, 2, 128, 192, False, None),
+    (1, 3, 200, 64, True, None),
+    # key lengths with ties, an empty batch and an odd number of items (the
+    # pairs tiles rank batches by length and run the middle item alone)
+    (5, 3, 200, 300, False, [300, 17, 300, 0, 150]),
+    (3, 1, 100, 200, False, [5, 200, 100]),
 ]
 
 
-@pytest.fixture
-def forced_tile(request):
-    require_gpu()
-    old = os.environ.get("SDPA_FORCE_TILE")
-    os.environ["SDPA_FORCE_TILE"] = request.param
-    yield request.param
-    if old is None:
-        os.environ.pop("SDPA_FORCE_TILE", None)
-    else:
-        os.environ["SDPA_FORCE_TILE"] = old
-
-
-def _check_selected(d, tile):
+def run_tile(q, k, v, causal, key_lens, tile):
     import torch
     import transformer_scaled_dot_sdpa_amd as sdpa
-    q = torch.empty((1, 1, 8, d), dtype=torch.bfloat16, device="cuda")
-    assert sdpa.kernel_name(q, q, False, False) == tile
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    kl = torch.from_numpy(np.asarray(key_lens, dtype=np.int32)).cuda() if key_lens is not None else None
+    out, lse = sdpa.forward_ex(qd, kd, vd, causal=causal, key_lens=kl, tile=tile)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("d,forced_tile", TILE_PARAMS, indirect=["forced_tile"],
-                         ids=[t for _, t in TILE_PARAMS])
+@pytest.mark.parametrize("d,tile", TILE_PARAMS, ids=[t for _, t in TILE_PARAMS])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}q{}k{}c{}L{}".format(*c[:5], c[5]))
-def test_tile_matches_oracle(d, forced_tile, case):
-    _check_selected(d, forced_tile)
+def test_tile_matches_oracle(d, tile, case):
+    require_gpu()
     B, H, Lq, Lk, causal, kl = case
     seed = 500 + d + Lq + 3 * Lk
-    announce(f"tile {forced_tile}: B{B} H{H} Lq{Lq} Lk{Lk} causal={causal} key_lens={kl} seed={seed}")
+    announce(f"tile {tile}: B{B} H{H} Lq{Lq} Lk{Lk} causal={causal} key_lens={kl} seed={seed}")
     q, k, v, _ = generate(B, H, Lq, Lk, d, "bf16", seed)
-    o, l = run_gpu(q, k, v, "bf16", causal, kl)
+    o, l = run_tile(q, k, v, causal, kl, tile)
     ro, rl = oracle_ref(q, k, v, "bf16", causal, kl)
-    assert_close(o, l, ro, rl, "bf16", f"{forced_tile} {case}")
+    assert_close(o, l, ro, rl, "bf16", f"{tile} {case}")
     if kl is not None:
         for b, n in enumerate(kl):
             if n <= 0:
                 assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
 
 
-@pytest.mark.parametrize("d,forced_tile", TILE_PARAMS, indirect=["forced_tile"],
-                         ids=[t for _, t in TILE_PARAMS])
+@pytest.mark.parametrize("d,tile", TILE_PARAMS, ids=[t for _, t in TILE_PARAMS])
 @pytest.mark.parametrize("causal", [False, True])
-def test_tile_scores_growing_along_keys(d, forced_tile, causal):
+def test_tile_scores_growing_along_keys(d, tile, causal):
     """Batch 0: scores rise with the key index far past the first tile's
     maximum; batch 1: random rows in the same launch."""
-    _check_selected(d, forced_tile)
+    require_gpu()
     B, H, L = 2, 2, 512
     q, k, v, _ = generate(B, H, L, L, d, "bf16", 31 + d)
     qf = np.zeros((H, L, d), np.float32)
@@ -89,7 +83,51 @@ def test_tile_scores_growing_along_keys(d, forced_tile, causal):
     kf[:, :, 0] = (0.25 if d == 128 else 0.125) * np.arange(L)[None, :]
     q[0] = inputs.f32_to_bf16_bits(qf)
     k[0] = inputs.f32_to_bf16_bits(kf)
-    announce(f"tile {forced_tile}: growing scores causal={causal}")
-    o, l = run_gpu(q, k, v, "bf16", causal)
+    announce(f"tile {tile}: growing scores causal={causal}")
+    o, l = run_tile(q, k, v, causal, None, tile)
     ro, rl = oracle_ref(q, k, v, "bf16", causal)
-    assert_close(o, l, ro, rl, "bf16", f"{forced_tile} growing causal={causal}")
+    assert_close(o, l, ro, rl, "bf16", f"{tile} growing causal={causal}")
+
+
+@pytest.mark.parametrize("d,tile", TILE_PARAMS, ids=[t for _, t in TILE_PARAMS])
+def test_tile_bitwise_deterministic(d, tile):
+    """Two runs of one tile give the same bits (no atomics, fixed orders)."""
+    require_gpu()
+    q, k, v, _ = generate(2, 3, 333, 400, d, "bf16", 77 + d)
+    announce(f"tile {tile}: determinism")
+    o1, l1 = run_tile(q, k, v, True, [250, 400], tile)
+    o2, l2 = run_tile(q, k, v, True, [250, 400], tile)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_tile_names_and_refusals():
+    """Unknown names and non-default tiles asked for a mask or d_v != d_k are
+    refused with NOT_SUPPORTED; the selector's names are compiled tiles."""
+    require_gpu()
+    import torch
+    import transformer_scaled_dot_sdpa_amd as sdpa
+    from transformer_scaled_dot_sdpa_amd.binding import NOT_SUPPORTED, SdpaError
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    v128 = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
+    mask = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
+    for bad in ("bf16_d64_nope", "bf16_d128_bc64_w4", "bf16_d64_bc128_w4"):
+        with pytest.raises(SdpaError) as e:
+            sdpa.forward_ex(q, q, q, tile=bad)
+        assert e.value.status == NOT_SUPPORTED
+    with pytest.raises(SdpaError) as e:
+        sdpa.forward_ex(q, q, q, mask=mask, tile="bf16_d64_bc64_w8")
+    assert e.value.status == NOT_SUPPORTED
+    with pytest.raises(SdpaError) as e:
+        sdpa.forward_ex(q, q, v128, tile="bf16_d64_bc64_w8")
+    assert e.value.status == NOT_SUPPORTED
+    sdpa.forward_ex(q, q, q, mask=mask, tile="bf16_d64_bc64_w4")
+    sdpa.forward_ex(q, q, v128, tile="bf16_d64_bc64_w4")
+    sdpa.forward_ex(q, q, v128, mask=mask, tile="bf16_d64_bc64_w4_pairs")
+    torch.cuda.synchronize()
+    for (B, H, Lq, Lk, d, causal) in [(4, 96, 4096, 4096, 128, True), (64, 8, 128, 128, 64, False),
+                                      (32, 8, 256, 256, 64, True), (32, 8, 256, 512, 64, False),
+                                      (1, 8, 1, 4096, 64, False)]:
+        qq = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device="meta")
+        kk = torch.empty((B, H, Lk, d), dtype=torch.bfloat16, device="meta")
+        name = sdpa.binding.sdpa_kernel_name(sdpa.binding.handle_for(1, 0), B, H, Lq, Lk, d, causal, False)
+        assert name in TILES[d], name

@@ -40,7 +40,7 @@ class ForwardDesc(ctypes.Structure):
                 ("q_layout", Layout), ("k_layout", Layout), ("v_layout", Layout),
                 ("out_layout", Layout), ("causal", ctypes.c_int),
                 ("key_lens", ctypes.c_void_p), ("scale", ctypes.c_float),
-                ("mask", ctypes.c_void_p), ("mask_layout", Layout)]
+                ("mask", ctypes.c_void_p), ("mask_layout", Layout), ("tile", ctypes.c_char_p)]
 
 
 class SdpaError(RuntimeError):
@@ -242,15 +242,16 @@ def _layout_of(t, name):
 
 
 def forward_ex(q, k, v, causal: bool = False, key_lens=None, scale=None, mask=None, out=None,
-               lse=None, need_lse: bool = True, stream=None):
+               lse=None, need_lse: bool = True, stream=None, tile=None):
     """General forward: ``q``, ``k`` ([.., d_k]) and ``v`` ([.., d_v]) are
     [B, H, L, width] views with any strides whose last dimension is
     contiguous -- e.g. ``x.view(B, L, H, d).transpose(1, 2)`` for the
     head-interleaved [B, L, H*d] layout.  ``scale`` multiplies q.k (default
     1/sqrt(d_k)); ``mask`` is an additive float32 tensor broadcastable to
     [B, H, Lq, Lk] (last dimension contiguous; -inf drops a key).  ``out``
-    may be a preallocated [B, H, Lq, d_v] view of any strides.  Returns
-    ``(out, lse)``."""
+    may be a preallocated [B, H, Lq, d_v] view of any strides.  ``tile``
+    names a compiled tile configuration (see :func:`kernel_name`) to run
+    instead of the one chosen by shape.  Returns ``(out, lse)``."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -298,6 +299,7 @@ def forward_ex(q, k, v, causal: bool = False, key_lens=None, scale=None, mask=No
             raise ValueError("mask rows must not be broadcast")
         desc.mask = mv.data_ptr()
         desc.mask_layout = ml
+    desc.tile = tile.encode() if tile is not None else None
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = sdpa_forward_ex(handle_for(code, dev), desc, stream.cuda_stream)

@@ -9,6 +9,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -52,6 +53,51 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+# Global-memory instructions each forward kernel may contain: Q fragment
+# loads (16 bytes per k-step pair), two key-length loads (the item's, and the
+# ranking of batches by length), O stores (8 bytes per lane and 4 output
+# columns) and one lse store.  Anything else -- a flat
+# access, or more global accesses than these -- means an LDS access was
+# compiled as a global one (an LDS address used as a global address faults
+# the GPU), so the build refuses it.
+_FWD_KERNEL = re.compile(r"^(_ZN4sdpa12_GLOBAL__N_115fwd_bf16_kernelILi(\d+)ELi(\d+)ELi\d+ELi\d+ELi\d+ELb([01])ELb([01])ELb([01])E\w*):",
+                         re.M)
+
+
+def audit_forward_isa(src: str | None = None) -> int:
+    """Compile the forward kernels to gfx950 assembly and check every
+    instance's global and flat memory instructions against the expected
+    set; returns the number of kernels checked, raises on a mismatch."""
+    src = src or os.path.join(CSRC, "sdpa_fwd_bf16.hip")
+    os.makedirs(BUILD, exist_ok=True)
+    asm = os.path.join(BUILD, "sdpa_fwd_bf16.audit.s")
+    cmd = [HIPCC, *COMMON, *EXTRA, "--cuda-device-only", "-S", src, "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    text = open(asm).read()
+    bad, n = [], 0
+    for m in _FWD_KERNEL.finditer(text):
+        name, d, dv, lens = m.group(1), int(m.group(2)), int(m.group(3)), m.group(5) == "1"
+        body = text[m.end():text.index(".Lfunc_end", m.end())]
+        ops = re.findall(r"^\s+((?:global|flat)_\w+)", body, re.M)
+        expect = {"global_load_dwordx4": d // 16, "global_store_dwordx2": 4 * (dv // 32),
+                  "global_store_dword": 1}
+        if lens:
+            expect["global_load_dword"] = 2
+        got = {}
+        for op in ops:
+            got[op] = got.get(op, 0) + 1
+        if got != expect:
+            bad.append(f"{name}: {got} (expected {expect})")
+        n += 1
+    if n == 0:
+        raise RuntimeError("no forward kernel found in the assembly")
+    if bad:
+        raise RuntimeError("forward kernels with unexpected global/flat memory instructions:\n" + "\n".join(bad))
+    return n
+
+
 def build(verbose: bool = False, out: str | None = None, build_dir: str | None = None) -> str:
     """Compile every source under ``csrc/`` and link the shared library
     (to ``out``, default ``lib/libsdpa_mi355x.so``)."""
@@ -62,8 +108,10 @@ def build(verbose: bool = False, out: str | None = None, build_dir: str | None =
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(os.path.dirname(lib), exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        audit = ex.submit(audit_forward_isa)
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        audit.result()
     tmp = lib + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -38,9 +38,12 @@ struct KParams {
     int num_items;     // work items = (b, h, query block) triples
     int upi;           // work items per scheduling unit (1, or 2: a long/short pair)
     int num_units;     // ceil(num_items / upi)
+    int B;
+    // key-length pairs (LENS kernels): batches ordered by clamped key length,
+    // longest first, and unit u runs items u and num_items - 1 - u
+    int lens_pairs;
     float scale_log2;  // log2(e) * scale (scale = 1 / sqrt(d) unless given)
-    // Element strides of the [B, H, L, width] views (the main kernel only;
-    // the other kernels take contiguous tensors): batch, head, row.
+    // Element strides of the [B, H, L, width] views: batch, head, row.
     long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
     int q_sl, k_sl, v_sl, o_sl;
     // Additive fp32 mask on the scaled scores (MASK kernels): [B, H, Lq, Lk]

@@ -70,6 +70,27 @@ bool resolve_view(const sdpa_layout_t& lay, long long B, long long H, long long 
     return true;
 }
 
+// true if no two elements of the view share an address: every dimension of
+// size > 1 has a nonzero stride, and taken in increasing stride order each
+// stride is at least the span of the dimensions before it (width elements
+// for the contiguous last dimension).
+bool one_to_one(const View& v, long long B, long long H, long long L, long long width) {
+    struct Dim { long long n, st; };
+    Dim dims[3] = {{B, v.sb}, {H, v.sh}, {L, v.sl}};
+    for (const Dim& d : dims)
+        if (d.n > 1 && d.st == 0) return false;
+    // sort the three by stride (insertion sort)
+    for (int i = 1; i < 3; ++i)
+        for (int j = i; j > 0 && dims[j].st < dims[j - 1].st; --j) std::swap(dims[j], dims[j - 1]);
+    long long span = width;
+    for (const Dim& d : dims) {
+        if (d.n <= 1) continue;
+        if (d.st < span) return false;
+        span += (d.n - 1) * d.st;   // no overflow: the extent was checked by resolve_view
+    }
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,11 +139,11 @@ const char* sdpa_status_string(sdpa_status_t s) {
 
 const char* sdpa_kernel_name(sdpa_handle_t h, int B, int H, int Lq, int Lk, int d_k,
                              int causal, int has_key_lens) {
-    (void)has_key_lens;
     if (h == nullptr || B < 1 || H < 1 || Lq < 1 || Lk < 1 || d_k < 1) return nullptr;
     if (h->dtype == SDPA_DTYPE_FP32) return d_k <= 256 ? "f32_wave_per_row" : nullptr;
     sdpa::Bf16Tile t;
-    if (!sdpa::select_bf16_tile(d_k, causal, (long long)B * H, Lq, Lk, h->num_cus, &t)) return nullptr;
+    if (!sdpa::select_bf16_tile(d_k, causal, has_key_lens, (long long)B * H, Lq, Lk, h->num_cus, false, &t))
+        return nullptr;
     return t.name;
 }
 
@@ -158,7 +179,8 @@ sdpa_status_t sdpa_forward(sdpa_handle_t h, const void* q, const void* k, const 
 
     sdpa::Bf16Tile tile;
     if (h->dtype == SDPA_DTYPE_BF16) {
-        if (!sdpa::select_bf16_tile(d_k, causal, (long long)B * H, Lq, Lk, h->num_cus, &tile))
+        if (!sdpa::select_bf16_tile(d_k, causal, key_lens != nullptr, (long long)B * H, Lq, Lk, h->num_cus,
+                                    false, &tile))
             return SDPA_STATUS_NOT_SUPPORTED;
         for (const void* p : {q, k, v, (const void*)out})
             if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return SDPA_STATUS_NOT_SUPPORTED;
@@ -271,6 +293,9 @@ sdpa_status_t sdpa_forward_ex(sdpa_handle_t h, const sdpa_forward_desc_t* desc, 
         !resolve_view(d.v_layout, d.B, d.H, d.Lk, dv, &vv) ||
         !resolve_view(d.out_layout, d.B, d.H, d.Lq, dv, &vo))
         return SDPA_STATUS_INVALID_VALUE;
+    // several (b, h, row) of out at one address would be written by several
+    // workgroups at once
+    if (!one_to_one(vo, d.B, d.H, d.Lq, dv)) return SDPA_STATUS_INVALID_VALUE;
     if (d.mask != nullptr) {
         sdpa_layout_t ml = d.mask_layout;
         if (ml.row == 0) ml.row = d.Lk;   // all zero: one shared [Lq, Lk] matrix
@@ -300,8 +325,19 @@ sdpa_status_t sdpa_forward_ex(sdpa_handle_t h, const sdpa_forward_desc_t* desc, 
     if (d.mask != nullptr && reinterpret_cast<uintptr_t>(d.mask) % alignof(float) != 0)
         return SDPA_STATUS_INVALID_VALUE;
 
+    sdpa::Bf16Tile tile{};
     if (bf16) {
         if ((d.d_k != 64 && d.d_k != 128) || (dv != 64 && dv != 128)) return SDPA_STATUS_NOT_SUPPORTED;
+        // d_v != d_k and the additive mask are compiled into the default tile only
+        const bool general = dv != d.d_k || d.mask != nullptr;
+        if (d.tile != nullptr) {
+            if (!sdpa::find_bf16_tile(d.d_k, d.tile, &tile)) return SDPA_STATUS_NOT_SUPPORTED;
+            // the default geometry (64 keys, 4 wavefronts, no key split)
+            if (general && (tile.bc != 64 || tile.waves != 4 || tile.ks != 1)) return SDPA_STATUS_NOT_SUPPORTED;
+        } else {
+            sdpa::select_bf16_tile(d.d_k, d.causal, d.key_lens != nullptr, (long long)d.B * d.H, d.Lq, d.Lk,
+                                   h->num_cus, general, &tile);
+        }
         for (const void* p : {d.q, d.k, d.v, (const void*)d.out})
             if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return SDPA_STATUS_NOT_SUPPORTED;
         for (const View* v : {&vq, &vk, &vv, &vo})
@@ -314,6 +350,7 @@ sdpa_status_t sdpa_forward_ex(sdpa_handle_t h, const sdpa_forward_desc_t* desc, 
             return SDPA_STATUS_NOT_SUPPORTED;
     } else {
         if (d.d_k > 256 || dv > 256) return SDPA_STATUS_NOT_SUPPORTED;
+        if (d.tile != nullptr && strcmp(d.tile, "f32_wave_per_row") != 0) return SDPA_STATUS_NOT_SUPPORTED;
         for (const void* p : {d.q, d.k, d.v, (const void*)d.out})
             if (reinterpret_cast<uintptr_t>(p) % alignof(float) != 0) return SDPA_STATUS_INVALID_VALUE;
         for (const View* v : {&vq, &vk, &vv, &vo})
@@ -345,9 +382,6 @@ sdpa_status_t sdpa_forward_ex(sdpa_handle_t h, const sdpa_forward_desc_t* desc, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (bf16) {
-        // the main kernel's default tile: the one kernel with strides, d_v,
-        // scale and mask
-        const sdpa::Bf16Tile tile{d.d_k, 64, 4, 0, nullptr};
         e = sdpa::launch_fwd_bf16(a, tile, s);
     } else {
         e = sdpa::launch_fwd_f32(a, s);

@@ -378,7 +378,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& plan, hipSt
         f.B = a.B; f.H = a.H; f.Lq = a.Lq; f.Lk = a.Lk; f.d = a.d; f.causal = a.causal;
         f.num_cus = a.num_cus;
         f.set_contiguous();
-        const Bf16Tile tile{a.d, 64, 4, 0, nullptr};
+        const Bf16Tile tile{a.d, 64, 4, 1, 0, nullptr};
         return launch_fwd_bf16(f, tile, s);
     }
     if (a.d == 128) return launch_d<128>(a, plan, s);

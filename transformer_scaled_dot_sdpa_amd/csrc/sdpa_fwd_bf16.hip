@@ -23,6 +23,14 @@
 //     Computing the transposed products keeps each query's running max/sum
 //     and its whole output column inside one lane pair, so the rescale of O
 //     is a per-lane multiply and the row reductions need one cross-lane swap.
+//   * key split (KS = 2): the workgroup holds two groups of NW wavefronts
+//     over the same query rows; group g takes key tiles g, g + 2, g + 4, ...
+//     with K/V buffers of its own, and at the end group 1 hands its (O, m, l)
+//     to group 0 through LDS, which merges them as
+//       m = max(m0, m1), O = 2^(m0-m) O0 + 2^(m1-m) O1, l likewise
+//     (exact by the same ratio identity).  When a problem has too few query
+//     blocks to fill the GPU but long key ranges (few heads, long
+//     sequences), its workgroups then finish in half the tile steps.
 //   * masking (causal: key j > query i; padding: j >= key length; ragged
 //     tails) only runs on tiles that cross a boundary; tiles entirely above
 //     the causal diagonal are neither loaded nor computed.  K/V come in with
@@ -53,9 +61,19 @@ using namespace bf16k;
 // D: width of queries and keys; DV: width of values and outputs.  MASK adds
 // an fp32 bias to the scaled scores.  Tensor rows are addressed through the
 // strides in KParams (contiguous or head-interleaved layouts alike).
-template <int D, int DV, int BC, int NW, bool CAUSAL, bool LENS, bool MASK>
-__global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
-    constexpr int NT = NW * 64;
+// Every tile configuration runs two wavefronts per SIMD (the second
+// __launch_bounds__ argument, which caps a wavefront at 256 registers):
+// 8 / (NW * KS) workgroups per compute unit, at least one.
+template <int NW, int KS>
+constexpr int fwd_blocks_per_cu() {
+    return 8 / (NW * KS) > 0 ? 8 / (NW * KS) : 1;
+}
+
+template <int D, int DV, int BC, int NW, int KS, bool CAUSAL, bool LENS, bool MASK>
+__global__ void __launch_bounds__(NW * KS * 64, 2)
+fwd_bf16_kernel(KParams p) {
+    static_assert(KS == 1 || KS == 2, "key split of 1 or 2 groups");
+    constexpr int NT = NW * 64;                // threads of one group
     constexpr int BR = NW * 32;
     constexpr int CPR = D / 8;                 // 16-byte chunks per key row
     constexpr int CPRV = DV / 8;               // 16-byte chunks per value row
@@ -69,16 +87,26 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     static_assert((BC * CPR) % NT == 0 && (BC * CPRV) % NT == 0, "tile must split evenly over threads");
     static_assert(BC % 32 == 0, "BC must be a multiple of 32");
 
-    // K and V tiles, double buffered.  Four separate arrays rather than one:
-    // the compiler can then tell that the direct-to-LDS loads into one buffer
-    // never alias the reads of the other, and does not make those reads wait
-    // for the loads in flight (the tile barrier provides the real ordering).
-    __shared__ __align__(16) uint16_t k_lds0[TILE], k_lds1[TILE], v_lds0[TILEV], v_lds1[TILEV];
+    // K and V tiles, double buffered (one pair of buffers per key-split
+    // group).  Four separate arrays rather than one: the compiler can then
+    // tell that the direct-to-LDS loads into one buffer never alias the
+    // reads of the other, and does not make those reads wait for the loads
+    // in flight (the tile barrier provides the real ordering).
+    __shared__ __align__(16) uint16_t k_lds0[KS * TILE], k_lds1[KS * TILE], v_lds0[KS * TILEV],
+        v_lds1[KS * TILEV];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    // wave index is uniform: keep it in a scalar register
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // wave indices are uniform: keep them in scalar registers.  grp: key-split
+    // group; wave: wavefront inside the group (its 32 query rows).
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave_all / NW);
+    const int wave = KS == 1 ? wave_all : __builtin_amdgcn_readfirstlane(wave_all - grp * NW);
+    // this group's K/V buffers
+    uint16_t* const kb0 = k_lds0 + grp * TILE;
+    uint16_t* const kb1 = k_lds1 + grp * TILE;
+    uint16_t* const vb0 = v_lds0 + grp * TILEV;
+    uint16_t* const vb1 = v_lds1 + grp * TILEV;
     const int n = lane & 31;   // query column inside the wave
     const int h = lane >> 5;   // which half of the 16-wide k slice
 
@@ -124,14 +152,50 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         }
     }
 
+    // ---- key-length pairs: rank the batches by clamped key length (longest
+    // first, ties by index) in LDS; position r of the order holds batch
+    // s_order[r].  Every workgroup ranks the (few) lengths itself.
+    __shared__ int s_len[LENS ? kMaxPairBatches : 1], s_order[LENS ? kMaxPairBatches : 1];
+    if (LENS && p.lens_pairs) {
+        for (int i = tid; i < p.B; i += NT * KS) {
+            const int L = p.key_lens[i];
+            s_len[i] = L < 0 ? 0 : (L > p.Lk ? p.Lk : L);
+        }
+        __syncthreads();
+        for (int i = tid; i < p.B; i += NT * KS) {
+            const int li = s_len[i];
+            int r = 0;
+            for (int j = 0; j < p.B; ++j) r += (s_len[j] > li) || (s_len[j] == li && j < i);
+            s_order[r] = i;
+        }
+        __syncthreads();
+    }
+
     // ---- the workgroup's work items, one after the other (see
     // workgroup_units and item_block for the schedule and the order)
     int unit_first, unit_step, unit_last;
     workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
     for (int unit = unit_first; unit < unit_last; unit += unit_step)
-    for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
+    for (int k_item = 0; k_item < p.upi; ++k_item) {
+    int item;
+    if (LENS && p.lens_pairs) {
+        // items u and num_items - 1 - u: a long one and a short one
+        item = k_item == 0 ? unit : p.num_items - 1 - unit;
+        if (k_item == 1 && item <= unit) break;   // the middle item of an odd count runs once
+    } else {
+        item = unit * p.upi + k_item;
+        if (item >= p.num_items) break;
+    }
     int bh, qb;
-    item_block<CAUSAL>(item, p.num_qb, &bh, &qb);
+    if (LENS && p.lens_pairs) {
+        const int per_b = p.H * p.num_qb;
+        const int r = item / per_b, rem = item - r * per_b;
+        const int hq = rem / p.num_qb;
+        bh = s_order[r] * p.H + hq;
+        qb = rem - hq * p.num_qb;
+    } else {
+        item_block<CAUSAL>(item, p.num_qb, &bh, &qb);
+    }
     const int b = bh / p.H;
     const int hh = bh - b * p.H;
     const int q0 = qb * BR;
@@ -144,6 +208,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     }
     const int kv_end = CAUSAL ? min(kv_len, q0 + BR) : kv_len;
     const int ntiles = (kv_end + BC - 1) / BC;
+    // tile steps of the workgroup; in step r group g takes tile r * KS + g
+    const int nsteps = (ntiles + KS - 1) / KS;
 
     const int q0w = q0 + wave * 32;
     const int qrow = q0w + n;
@@ -172,12 +238,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
     // around it and the surrounding MFMA code stays one block).
     auto load_k = [&](int t, int buf, int u) __attribute__((always_inline)) {
         const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * p.k_sl * 2;
-        lds_void* kd = (lds_void*)((buf ? k_lds1 : k_lds0) + (wave * KCH + u) * 64 * 8);
+        lds_void* kd = (lds_void*)((buf ? kb1 : kb0) + (wave * KCH + u) * 64 * 8);
         buffer_load_lds16(kg, t < 0 ? 0u : k_bytes, kd, k_boff[u], toff);
     };
     auto load_v = [&](int t, int buf, int u) __attribute__((always_inline)) {
         const uint32_t toff = (uint32_t)((t < 0 ? 0 : t) * BC) * p.v_sl * 2;
-        lds_void* vd = (lds_void*)((buf ? v_lds1 : v_lds0) + (wave * KCHV + u) * 64 * 8);
+        lds_void* vd = (lds_void*)((buf ? vb1 : vb0) + (wave * KCHV + u) * 64 * 8);
         buffer_load_lds16(vg, t < 0 ? 0u : v_bytes, vd, v_boff[u], toff);
     };
     auto issue_loads = [&](int t, int buf) __attribute__((always_inline)) {
@@ -288,10 +354,13 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
                 }
         }
 
-        // the transposed V reads of the first two key steps go out before
-        // the softmax, whose vector work covers their latency
+        // the transposed V reads of the first key steps go out before the
+        // softmax, whose vector work covers their latency
         constexpr int NSTEP = 2 * NKT;
-        i16x8 va[3][NDT];
+        // V operand reads run RA key steps ahead
+        constexpr int RA = 2;
+        constexpr int VA = RA + 1;
+        i16x8 va[VA][NDT];
         auto read_v = [&](int step, i16x8* dst) __attribute__((always_inline)) {
             const int roff = (step * 16) * DV;   // step = 2*kt + ksl
 #pragma unroll
@@ -303,18 +372,31 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
                 dst[dt] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
         };
-        read_v(0, va[0]);
-        read_v(1, va[1]);
+#pragma unroll
+        for (int st = 0; st < RA; ++st) read_v(st, va[st]);
 
         bf16x8 pb[NKT][2];
         if constexpr (decltype(FAST)::value) {
-            // fixed reference: weights 2^(s*sl - m_run), no maximum taken
+            // fixed reference: weights 2^(s*sl - m_run), no maximum taken.  A
+            // row whose earlier tiles were all masked (m_run still -inf: a
+            // mask that drops its first keys) takes this tile's maximum as
+            // its reference, exactly as the first tile does.
+            if (__ballot(m_run == -INFINITY) != 0ull) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+                mx = max_across_halves(mx);
+                if (m_run == -INFINITY) m_run = mx * sl;
+            }
+            const float mref = (m_run == -INFINITY) ? 0.f : m_run;
             float lsum = 0.f;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -m_run));
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl, -mref));
                     lsum += pv;
                     pb[kt][r >> 3][r & 7] = (__bf16)pv;
                 }
@@ -357,39 +439,50 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         // V loads of the next tile are spread over the steps.
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
-            if (st + 2 < NSTEP) read_v(st + 2, va[(st + 2) % 3]);
+            if (st + RA < NSTEP) read_v(st + RA, va[(st + RA) % VA]);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, va[st % 3][dt]), pb[st >> 1][st & 1], o[dt], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, va[st % VA][dt]), pb[st >> 1][st & 1], o[dt], 0, 0, 0);
 #pragma unroll
             for (int u = st * KCHV / NSTEP; u < (st + 1) * KCHV / NSTEP; ++u) load_v(lt, lb, u);
         }
     };
 
-    // ---- main loop.  First pass: tile 0 sets the reference maximum
-    // exactly, every later tile runs the branch-free fixed-reference softmax.
-    // If any of those tiles in the workgroup saw weights >= 2^64 (scores
-    // that far above the first tile's maximum), the whole workgroup starts
-    // over with the exact online softmax on every tile.  Tile t lives in
-    // LDS buffer t & 1; loops are unrolled by two so the offsets are
-    // constants.
+    // ---- main loop.  First pass: the first tile of each group sets the
+    // reference maximum exactly, every later tile runs the branch-free
+    // fixed-reference softmax.  If any of those tiles in the workgroup saw
+    // weights >= 2^64 (scores that far above the reference), the whole
+    // workgroup starts over with the exact online softmax on every tile.
+    // Step r uses LDS buffer r & 1; loops are unrolled by two so the offsets
+    // are constants.  In step r this group computes tile r * KS + grp (if it
+    // exists and reaches this wavefront's rows) and loads tile (r+1) * KS +
+    // grp (-1: none).
+    auto tile_of = [&](int r) __attribute__((always_inline)) {
+        const int t = r * KS + grp;
+        return t < ntiles ? t : -1;
+    };
     auto run_pass = [&](auto TAIL) __attribute__((always_inline)) {
-        issue_loads(0, 0);
+        issue_loads(tile_of(0), 0);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        tile_math(std::false_type(), 0, k_lds0, v_lds0, 1 < ntiles ? 1 : -1, 1);
-        for (int t = 1; t < ntiles; t += 2) {
+        {
+            const int t0 = tile_of(0);
+            if (t0 >= 0 && t0 * BC < wave_kv_end)
+                tile_math(std::false_type(), t0, kb0, vb0, tile_of(1), 1);
+            else if (tile_of(1) >= 0) issue_loads(tile_of(1), 1);
+        }
+        for (int r = 1; r < nsteps; r += 2) {
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
-            const int l0 = t + 1 < ntiles ? t + 1 : -1;
-            if (t * BC < wave_kv_end) tile_math(TAIL, t, k_lds1, v_lds1, l0, 0);
+            const int c0 = tile_of(r), l0 = r + 1 < nsteps ? tile_of(r + 1) : -1;
+            if (c0 >= 0 && c0 * BC < wave_kv_end) tile_math(TAIL, c0, kb1, vb1, l0, 0);
             else if (l0 >= 0) issue_loads(l0, 0);
-            if (t + 1 >= ntiles) break;
+            if (r + 1 >= nsteps) break;
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
-            const int l1 = t + 2 < ntiles ? t + 2 : -1;
-            if ((t + 1) * BC < wave_kv_end) tile_math(TAIL, t + 1, k_lds0, v_lds0, l1, 1);
+            const int c1 = tile_of(r + 1), l1 = r + 2 < nsteps ? tile_of(r + 2) : -1;
+            if (c1 >= 0 && c1 * BC < wave_kv_end) tile_math(TAIL, c1, kb0, vb0, l1, 1);
             else if (l1 >= 0) issue_loads(l1, 1);
         }
         // zero-length loads of the last tile may still be in flight
@@ -408,10 +501,65 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         }
     }
 
-    // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l)
+    // ---- key split: group 1 hands (O, m, l) to group 0 through LDS (the
+    // K/V buffers, free once every wavefront has passed the barrier below),
+    // lane for lane: both groups hold the same rows in the same lanes.
+    if constexpr (KS == 2) {
+        constexpr int CHUNK = NW * 16 * 64;          // floats of one dt block of O
+        constexpr int CAP_K = KS * TILE * 2 / (CHUNK * 4);
+        constexpr int CAP_V = KS * TILEV * 2 / (CHUNK * 4);
+        static_assert(2 * CAP_K + 2 * CAP_V >= NDT + 1, "LDS too small for the key-split exchange");
+        // chunk c (c < NDT: O block dt = c; c = NDT: m and l) -> LDS address.
+        // The pointers are typed as LDS (address space 3): through generic
+        // pointers the compiler may lose the address space and emit global
+        // accesses at LDS addresses.
+        typedef __attribute__((address_space(3))) float lds_f32;
+        auto xch = [&](int c) __attribute__((always_inline)) -> lds_f32* {
+            return c < CAP_K             ? (lds_f32*)k_lds0 + c * CHUNK
+                   : c < 2 * CAP_K         ? (lds_f32*)k_lds1 + (c - CAP_K) * CHUNK
+                   : c < 2 * CAP_K + CAP_V ? (lds_f32*)v_lds0 + (c - 2 * CAP_K) * CHUNK
+                                           : (lds_f32*)v_lds1 + (c - 2 * CAP_K - CAP_V) * CHUNK;
+        };
+        __syncthreads();
+        const int li64 = wave * 16 * 64 + lane;
+        if (grp == 1) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                lds_f32* dst = xch(dt);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[li64 + r * 64] = o[dt][r];
+            }
+            lds_f32* ml = xch(NDT);
+            ml[wave * 128 + lane] = m_run;
+            ml[wave * 128 + 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (grp == 0) {
+            const lds_f32* ml = xch(NDT);
+            const float m1 = ml[wave * 128 + lane];
+            const float l1 = ml[wave * 128 + 64 + lane];
+            const float mn = fmaxf(m_run, m1);
+            // a group that saw no valid key has m = -inf and weight 0
+            const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const lds_f32* src = xch(dt);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * a0 + src[li64 + r * 64] * a1;
+            }
+            l_run = l_run * a0 + l1 * a1;
+            m_run = mn;
+        }
+    }
+
+    // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l).  Plain stores:
+    // each instruction writes 16 bytes of 32 rows, partial cache lines that
+    // L2 merges into whole lines; non-temporal stores of the same pattern
+    // made the short workloads 70-85% slower on MI355X.
     const float l = sum_across_halves(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (qrow < p.Lq) {
+    if (grp == 0 && qrow < p.Lq) {
         uint16_t* dst = p.out + b * p.o_sb + hh * p.o_sh + (size_t)qrow * p.o_sl;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -426,16 +574,16 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) fwd_bf16_kernel(KParams p) {
         if (p.lse != nullptr && h == 0)
             p.lse[(size_t)bh * p.Lq + qrow] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
     }
-    // every wavefront is done with both LDS buffers before the next item's
+    // every wavefront is done with the LDS buffers before the next item's
     // first loads overwrite them
     __syncthreads();
     }
 }
 
-template <int D, int DV, int BC, int NW, bool CAUSAL, bool LENS, bool MASK>
-hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
+template <int D, int DV, int BC, int NW, int KS, bool CAUSAL, bool LENS, bool MASK>
+hipError_t launch_one(const FwdArgs& a, bool pairs, hipStream_t stream) {
     constexpr int BR = NW * 32;
-    auto kern = fwd_bf16_kernel<D, DV, BC, NW, CAUSAL, LENS, MASK>;
+    auto kern = fwd_bf16_kernel<D, DV, BC, NW, KS, CAUSAL, LENS, MASK>;
     KParams p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -466,51 +614,55 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     // long/short pairs of equal length once there are more items than
     // resident workgroups; a smaller problem takes one item per workgroup so
     // that every item starts at once.
-    const long long slots = (long long)(a.num_cus > 0 ? a.num_cus : 256) * (8 / NW);
+    const long long slots = (long long)(a.num_cus > 0 ? a.num_cus : 256) * fwd_blocks_per_cu<NW, KS>();
     p.upi = (CAUSAL && items > slots) ? 2 : 1;
+    p.B = a.B;
+    p.lens_pairs = 0;
+    if (LENS && !CAUSAL && pairs && a.B > 1 && a.B <= kMaxPairBatches) {
+        p.lens_pairs = 1;
+        p.upi = 2;
+    }
     p.num_units = (int)((items + p.upi - 1) / p.upi);
     const long long nwg = p.num_units;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * KS * 64), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, int DV, int BC, int NW, bool MASK>
-hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
+template <int D, int DV, int BC, int NW, int KS, bool MASK>
+hipError_t launch_d(const FwdArgs& a, bool pairs, hipStream_t s) {
     const bool lens = a.key_lens != nullptr;
     if (a.causal)
-        return lens ? launch_one<D, DV, BC, NW, true, true, MASK>(a, s)
-                    : launch_one<D, DV, BC, NW, true, false, MASK>(a, s);
-    return lens ? launch_one<D, DV, BC, NW, false, true, MASK>(a, s)
-                : launch_one<D, DV, BC, NW, false, false, MASK>(a, s);
+        return lens ? launch_one<D, DV, BC, NW, KS, true, true, MASK>(a, pairs, s)
+                    : launch_one<D, DV, BC, NW, KS, true, false, MASK>(a, pairs, s);
+    return lens ? launch_one<D, DV, BC, NW, KS, false, true, MASK>(a, pairs, s)
+                : launch_one<D, DV, BC, NW, KS, false, false, MASK>(a, pairs, s);
 }
 
-// default tiles (64 keys, 4 wavefronts) for every (d_k, d_v) pair, with and
-// without the additive mask
+// default tiles (64 keys, 4 wavefronts, no key split) for every (d_k, d_v)
+// pair, with and without the additive mask
 template <int D, int DV>
-hipError_t launch_default(const FwdArgs& a, hipStream_t s) {
-    return a.mask != nullptr ? launch_d<D, DV, 64, 4, true>(a, s) : launch_d<D, DV, 64, 4, false>(a, s);
+hipError_t launch_default(const FwdArgs& a, bool pairs, hipStream_t s) {
+    return a.mask != nullptr ? launch_d<D, DV, 64, 4, 1, true>(a, pairs, s)
+                             : launch_d<D, DV, 64, 4, 1, false>(a, pairs, s);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s) {
-    if (t.kind == 1) return launch_fwd_bf16_pipe(a, t, s);
-    if (t.kind == 2) return launch_fwd_bf16_pp(a, t, s);
-    if (t.kind == 3) return launch_fwd_bf16_wide(a, t, s);
-    if (t.kind == 4) return launch_fwd_bf16_mix(a, t, s);
     if (t.d != a.d) return hipErrorInvalidValue;
-    if (t.bc == 64 && t.waves == 4) {
-        if (a.d == 128 && a.dv == 128) return launch_default<128, 128>(a, s);
-        if (a.d == 128 && a.dv == 64) return launch_default<128, 64>(a, s);
-        if (a.d == 64 && a.dv == 64) return launch_default<64, 64>(a, s);
-        if (a.d == 64 && a.dv == 128) return launch_default<64, 128>(a, s);
+    const bool pairs = t.pairs != 0;
+    if (t.bc == 64 && t.waves == 4 && t.ks == 1) {
+        if (a.d == 128 && a.dv == 128) return launch_default<128, 128>(a, pairs, s);
+        if (a.d == 128 && a.dv == 64) return launch_default<128, 64>(a, pairs, s);
+        if (a.d == 64 && a.dv == 64) return launch_default<64, 64>(a, pairs, s);
+        if (a.d == 64 && a.dv == 128) return launch_default<64, 128>(a, pairs, s);
         return hipErrorInvalidValue;
     }
     // the other tiles: d_v = d_k, no mask
     if (a.dv != a.d || a.mask != nullptr) return hipErrorInvalidValue;
-    if (t.d == 128 && t.bc == 64 && t.waves == 8) return launch_d<128, 128, 64, 8, false>(a, s);
-    if (t.d == 64 && t.bc == 128 && t.waves == 4) return launch_d<64, 64, 128, 4, false>(a, s);
-    if (t.d == 64 && t.bc == 64 && t.waves == 8) return launch_d<64, 64, 64, 8, false>(a, s);
+    if (t.d == 128 && t.bc == 64 && t.waves == 4 && t.ks == 2) return launch_d<128, 128, 64, 4, 2, false>(a, pairs, s);
+    if (t.d == 128 && t.bc == 64 && t.waves == 8 && t.ks == 1) return launch_d<128, 128, 64, 8, 1, false>(a, pairs, s);
+    if (t.d == 64 && t.bc == 64 && t.waves == 8 && t.ks == 1) return launch_d<64, 64, 64, 8, 1, false>(a, pairs, s);
     return hipErrorInvalidValue;
 }
 

@@ -10,9 +10,9 @@ namespace sdpa {
 // Arguments shared by every forward kernel.  q/k/v/out are [B, H, L, width]
 // views (q/out with L = Lq, k/v with L = Lk; width d for q/k, dv for v/out)
 // given by element strides of batch, head and row; the last dimension is
-// contiguous.  lse is contiguous [B, H, Lq].  Only the main bf16 kernel and
-// the fp32 kernel honour strides, dv != d, scale and mask; the other bf16
-// kernels take the contiguous defaults (set_contiguous).
+// contiguous.  lse is contiguous [B, H, Lq].  The bf16 kernel's default
+// tile and the fp32 kernel honour strides, dv != d, scale and mask; the
+// other bf16 tiles take dv = d and no mask.
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -93,28 +93,34 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int B, int H, int Lq, int Lk, int d, int num_cus);
 
-// One bf16 tile configuration.  br = rows of Q per workgroup
-// (32 per wavefront), bc = keys per K/V tile.
+// One bf16 tile configuration of the forward kernel (sdpa_fwd_bf16.hip):
+// waves wavefronts of 32 query rows each share K/V tiles of bc keys; with
+// ks = 2 two such groups take alternate key tiles of the same rows.  pairs:
+// with per-batch key lengths (and no causal mask) each workgroup runs a
+// long item and a short one, batches ranked by key length.
 struct Bf16Tile {
     int d;
     int bc;
     int waves;
-    int kind;   // 0: sdpa_fwd_bf16.hip, 1: sdpa_fwd_bf16_pipe.hip, 2: sdpa_fwd_bf16_pp.hip,
-                // 3: sdpa_fwd_bf16_wide.hip, 4: sdpa_fwd_bf16_mix.hip
+    int ks;
+    int pairs;
     const char* name;
 };
 
-// Picks the bf16 tile for a problem (tile_select.cpp).  Returns false if
-// d is not one of the compiled head sizes.
-bool select_bf16_tile(int d, int causal, long long bh, int Lq, int Lk, int num_cus,
-                      Bf16Tile* out);
+// Most batches the key-length ranking takes (LDS arrays of the kernel).
+constexpr int kMaxPairBatches = 512;
+
+// Picks the bf16 tile for a problem (tile_select.cpp).  general: the call
+// has d_v != d_k or an additive mask, which only the default tile takes.
+// Returns false if d is not one of the compiled head sizes.
+bool select_bf16_tile(int d, int causal, int has_key_lens, long long bh, int Lq, int Lk, int num_cus,
+                      bool general, Bf16Tile* out);
+// The compiled tile of this name and head size (tuning and tests); false if
+// there is none.
+bool find_bf16_tile(int d, const char* name, Bf16Tile* out);
 
 // Kernel launchers; return hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
-hipError_t launch_fwd_bf16_pipe(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
-hipError_t launch_fwd_bf16_pp(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
-hipError_t launch_fwd_bf16_wide(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
-hipError_t launch_fwd_bf16_mix(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s);

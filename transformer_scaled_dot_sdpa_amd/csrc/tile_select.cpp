@@ -3,10 +3,36 @@
 // Head sizes 64 (the base model's 8 heads of 64: cookipedia article
 // "Attention Is All You Need", section "原論文でのエンコーダ") and 128
 // (GPT-3's heads, formula page "トランスフォーマーの注意機構", section 起源)
-// are compiled.  The environment variable SDPA_FORCE_TILE may name one
-// compiled configuration (e.g. "bf16_d128_bc64_w4") to override the choice,
-// for tuning runs.
-#include <stdlib.h>
+// are compiled.  The choice depends on how the problem fills the GPU:
+//
+//   items  = B*H * ceil(Lq / 128)       query blocks of 128 rows
+//   cus    = compute units; the default tile keeps 2 workgroups per CU
+//   steps  = key tiles of 64 in a row's longest range (Lk; for causal,
+//            min(Lq, Lk))
+//
+//   bf16_d*_bc64_w4       default: 4 wavefronts (128 rows) per workgroup,
+//                         2 per CU; the only tile with d_v != d_k and masks
+//   bf16_d128_bc64_w4_ks2 two groups of 4 wavefronts take alternate key
+//                         tiles of the same 128 rows (1 workgroup per CU):
+//                         half the tile steps per item.  Wins when the
+//                         items are too few to keep the slots busy and
+//                         their key ranges are long: causal problems of at
+//                         most 2 items per CU with >= 32 steps (the longest
+//                         items set the time), non-causal ones of at most 1
+//                         item per CU with >= 16 steps.
+//   bf16_d*_bc64_w8       8 wavefronts (256 rows) share each K/V tile, 1
+//                         workgroup per CU: half the L2->LDS bytes per flop.
+//                         Wins for 2..4 items per CU with >= 16 steps (d64:
+//                         at most 64) and no key lengths.
+//   bf16_d*_bc64_w4_pairs per-batch key lengths, no causal mask: batches
+//                         ranked by length, each workgroup runs the i-th
+//                         longest and the i-th shortest item.  Wins when the
+//                         items need between one and two rounds of slots
+//                         (balanced pairs fill one round); loses when they
+//                         fit in one round (every item starts at once).
+//
+// The thresholds come from timing every tile on 36 shapes on MI355X
+// (interleaved batches, median of 3); the design notes list the table.
 #include <string.h>
 
 #include "sdpa_internal.h"
@@ -14,41 +40,51 @@
 namespace sdpa {
 
 namespace {
-// First entry per head size is the default.
+// Every compiled configuration; the first entry per head size is the default,
+// the only one that also takes d_v != d_k and an additive mask.
 const Bf16Tile kTiles[] = {
-    {128, 64, 4, 0, "bf16_d128_bc64_w4"},
-    {128, 64, 4, 1, "bf16_d128_pipe_w4"},
-    {128, 64, 8, 2, "bf16_d128_pp_w8"},
-    {128, 64, 8, 0, "bf16_d128_bc64_w8"},
-    {128, 64, 4, 3, "bf16_d128_wide_w4"},
-    {128, 64, 8, 4, "bf16_d128_mix_w8"},
-    {64, 64, 4, 0, "bf16_d64_bc64_w4"},
-    {64, 64, 4, 1, "bf16_d64_pipe_w4"},
-    {64, 64, 8, 2, "bf16_d64_pp_w8"},
-    {64, 128, 4, 0, "bf16_d64_bc128_w4"},
-    {64, 64, 8, 0, "bf16_d64_bc64_w8"},
-    {64, 64, 4, 3, "bf16_d64_wide_w4"},
-    {64, 64, 8, 4, "bf16_d64_mix_w8"},
+    {128, 64, 4, 1, 0, "bf16_d128_bc64_w4"},
+    {128, 64, 4, 1, 1, "bf16_d128_bc64_w4_pairs"},
+    {128, 64, 4, 2, 0, "bf16_d128_bc64_w4_ks2"},
+    {128, 64, 8, 1, 0, "bf16_d128_bc64_w8"},
+    {64, 64, 4, 1, 0, "bf16_d64_bc64_w4"},
+    {64, 64, 4, 1, 1, "bf16_d64_bc64_w4_pairs"},
+    {64, 64, 8, 1, 0, "bf16_d64_bc64_w8"},
 };
+
+const Bf16Tile* tile_named(int d, const char* name) {
+    for (const Bf16Tile& t : kTiles)
+        if (t.d == d && strcmp(name, t.name) == 0) return &t;
+    return nullptr;
+}
 }  // namespace
 
-bool select_bf16_tile(int d, int causal, long long bh, int Lq, int Lk, int num_cus,
-                      Bf16Tile* out) {
-    (void)causal; (void)bh; (void)Lq; (void)Lk; (void)num_cus;
-    const char* force = getenv("SDPA_FORCE_TILE");
-    if (force != nullptr && force[0] != '\0') {
-        for (const Bf16Tile& t : kTiles)
-            if (t.d == d && strcmp(force, t.name) == 0) {
-                *out = t;
-                return true;
-            }
+bool find_bf16_tile(int d, const char* name, Bf16Tile* out) {
+    if (name == nullptr) return false;
+    const Bf16Tile* t = tile_named(d, name);
+    if (t == nullptr) return false;
+    *out = *t;
+    return true;
+}
+
+bool select_bf16_tile(int d, int causal, int has_key_lens, long long bh, int Lq, int Lk, int num_cus,
+                      bool general, Bf16Tile* out) {
+    if (d != 64 && d != 128) return false;
+    const long long cus = num_cus > 0 ? num_cus : 256;
+    const long long items = bh * ((Lq + 127) / 128);
+    const long long steps = ((causal ? (Lq < Lk ? Lq : Lk) : Lk) + 63) / 64;
+    const char* name = d == 128 ? "bf16_d128_bc64_w4" : "bf16_d64_bc64_w4";
+    if (has_key_lens && !causal && items > 2 * cus && items <= 4 * cus) {
+        name = d == 128 ? "bf16_d128_bc64_w4_pairs" : "bf16_d64_bc64_w4_pairs";
+    } else if (!general && d == 128 && ((causal && items <= 2 * cus && steps >= 32) ||
+                                        (!causal && items <= cus && steps >= 16))) {
+        name = "bf16_d128_bc64_w4_ks2";
+    } else if (!general && !has_key_lens && items >= 2 * cus && items <= 4 * cus && steps >= 16 &&
+               (d == 128 || steps <= 64)) {
+        name = d == 128 ? "bf16_d128_bc64_w8" : "bf16_d64_bc64_w8";
     }
-    for (const Bf16Tile& t : kTiles)
-        if (t.d == d) {
-            *out = t;
-            return true;
-        }
-    return false;
+    *out = *tile_named(d, name);
+    return true;
 }
 
 }  // namespace sdpa
