@@ -32,10 +32,23 @@ in HBM.  W untimed steps, then K timed steps bracketed by
   the head-interleaved [B, L, H*d] layout, and with an additive fp32 bias
   (a [Lq, Lk] matrix shared by every slice) on top of the causal mask, each
   timed with HIP events and reported in TFLOP/s by the headline formula;
+* ``configs``: the other workloads of the benchmark set (toy fp32, encoder,
+  decoder causal, cross-attention with key lengths), each timed as batches
+  of 200 back-to-back calls between two HIP events on the launch stream,
+  with at least 8 input/output sets rotated (more than the 256 MiB
+  Infinity Cache together, so every call reads HBM); median of 5 batches,
+  and the same with one set (hot cache) reported apart.  µs per call,
+  TFLOP/s by the headline formula and algorithmic GB/s against 8 TB/s;
 * ``vendor_gemm``: context for the MFMA roofline -- the rate torch.matmul
   (the vendor BLAS) reaches on a large square bf16 product on the same GPU in
   the same run, i.e. what dense matrix cores deliver in practice at the clock
   the chip holds under full MFMA load, and ``value`` as a fraction of it.
+
+Before the W warm-up steps the GPU runs untimed calls for
+``--clock-settle`` seconds (default 0.25): its clock takes tens of
+milliseconds to ramp up from idle, which a handful of warm-up steps of the
+default workload does not cover.  ``--all`` prints one JSON line per
+workload instead (the main line first).
 
 Only one GPU is used; ``--gpus`` above 1 exits with a message.
 """
@@ -318,16 +331,26 @@ def forward_ex_leg(torch, sdpa, w, sets, tkl, stream, args):
                                                  lse=lse, stream=stream))
     ms_mask, _ = timed(lambda: sdpa.forward_ex(tq, tk, tv, causal=w.causal, key_lens=tkl, mask=bias,
                                                out=out, lse=lse, stream=stream))
+    # the same bias with every row's first 96 keys dropped (left padding):
+    # each row's first key tile is masked entirely, or nearly
+    bias_lp = bias.clone()
+    bias_lp[:, :96] = -math.inf
+    ms_lp, _ = timed(lambda: sdpa.forward_ex(tq, tk, tv, causal=w.causal, key_lens=tkl, mask=bias_lp,
+                                             out=out, lse=lse, stream=stream))
     tf = lambda ms: w.flops / (ms * 1e-3) / 1e12
     print(f"[bench] forward_ex: interleaved {ms_il*1e3:.1f} us ({tf(ms_il):.1f} TFLOP/s), "
-          f"with bias {ms_mask*1e3:.1f} us ({tf(ms_mask):.1f} TFLOP/s)", file=sys.stderr, flush=True)
-    del iq, ik, iv, iout, bias, out, lse
+          f"with bias {ms_mask*1e3:.1f} us ({tf(ms_mask):.1f} TFLOP/s), left-padded bias "
+          f"{ms_lp*1e3:.1f} us", file=sys.stderr, flush=True)
+    del iq, ik, iv, iout, bias, bias_lp, out, lse
     return {"steps": steps,
             "interleaved": {"layout": "[B, L, H*d_k] for q, k, v and out", "us_per_call": ms_il * 1e3,
                             "value": tf(ms_il), "unit": "TFLOP/s"},
             "additive_bias": {"mask": "fp32 [Lq, Lk] shared by every (b, h), plus the workload's masks",
                               "us_per_call": ms_mask * 1e3, "value": tf(ms_mask), "unit": "TFLOP/s",
-                              "mask_bytes": w.Lq * w.Lk * 4}}
+                              "mask_bytes": w.Lq * w.Lk * 4},
+            "additive_bias_left_padded": {"mask": "the same bias with keys 0..95 at -inf in every row",
+                                          "us_per_call": ms_lp * 1e3, "value": tf(ms_lp), "unit": "TFLOP/s",
+                                          "time_vs_additive_bias": ms_lp / ms_mask}}
 
 
 def decode_leg(torch, sdpa, inputs, name, args):
@@ -404,6 +427,77 @@ def decode_leg(torch, sdpa, inputs, name, args):
     return res
 
 
+SMALL_CONFIGS = ["toy_f32", "encoder_d64", "decoder_causal_d64", "cross_padded_d64"]
+
+
+def config_leg(torch, sdpa, inputs, name, batch=200, batches=5):
+    """One workload timed as batches of back-to-back sdpa_forward calls with
+    rotated input/output sets (see the module docstring)."""
+    import numpy as np
+    w = inputs.WORKLOADS[name]
+    print(f"[bench] config {w.name}: generating (seed {w.seed})", file=sys.stderr, flush=True)
+    q, k, v, kl = inputs.generate_workload(w)
+
+    def up(x):
+        t = torch.from_numpy(x)
+        return (t.view(torch.bfloat16) if w.dtype == "bf16" else t).cuda()
+
+    base = (up(q), up(k), up(v))
+    tkl = torch.from_numpy(kl).cuda() if kl is not None else None
+    flops_alg, bytes_alg = algorithmic_work(w, kl)
+    per_set = sum(t.numel() * t.element_size() for t in base) * 2 + w.B * w.H * w.Lq * 4
+    nsets = max(8, int(math.ceil((300 << 20) / per_set)))
+    sets = [tuple(t.clone() for t in base) + (torch.empty_like(base[0]),
+                                               torch.empty((w.B, w.H, w.Lq), dtype=torch.float32,
+                                                           device="cuda")) for _ in range(nsets)]
+    stream = torch.cuda.current_stream()
+
+    def call(a):
+        sdpa.forward(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=a[3], lse=a[4], stream=stream)
+
+    t_end = time.perf_counter() + 0.2
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(50):
+            call(sets[i % nsets])
+            i += 1
+        torch.cuda.synchronize()
+
+    def timed(rotate):
+        res = []
+        for _ in range(batches):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for j in range(batch):
+                call(sets[j % nsets] if rotate else sets[0])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e3 / batch)
+        return float(np.median(res)), res
+
+    us, all_us = timed(True)
+    us_hot, _ = timed(False)
+    gbs = bytes_alg / (us * 1e-6) / 1e9
+    out = {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d_k": w.d, "dtype": w.dtype,
+           "causal": w.causal, "key_lens": None if kl is None else "uniform[%d,%d]" % w.key_lens,
+           "seed": w.seed, "kernel": sdpa.kernel_name(base[0], base[1], w.causal, kl is not None),
+           "us_per_call": us, "us_per_call_batches": all_us, "us_per_call_hot_cache": us_hot,
+           "calls_per_batch": batch, "input_sets": nsets,
+           "value": w.flops / (us * 1e-6) / 1e12, "unit": "TFLOP/s",
+           "algorithmic_flops_per_call": flops_alg, "algorithmic_bytes_per_call": bytes_alg}
+    if w.dtype == "fp32":
+        out["roofline"] = {"bound": "latency", "note": f"{bytes_alg:.0f} B and {flops_alg:.0f} flop per call: "
+                           "the time is the launch; reported in us"}
+    else:
+        out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": gbs / PEAK_HBM_GBS}
+    print(f"[bench] config {w.name}: {us:.2f} us/call rotated, {us_hot:.2f} us hot, {gbs:.0f} GB/s, "
+          f"kernel {out['kernel']}", file=sys.stderr, flush=True)
+    del sets, base
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -422,6 +516,12 @@ def main():
                     help="skip the vendor GEMM context measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (toy, encoder, decoder, cross-attention)")
+    ap.add_argument("--all", action="store_true",
+                    help="print one JSON line per workload (the main line first)")
+    ap.add_argument("--clock-settle", type=float, default=0.25,
+                    help="seconds of untimed calls before the warm-up steps (clock ramp)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -473,24 +573,46 @@ def main():
         sdpa.forward(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=a[3], lse=a[4],
                      stream=stream)
 
-    print(f"[bench] warmup {args.warmup} steps, kernel {kname}, {nsets} input set(s)",
-          file=sys.stderr, flush=True)
+    settle_calls = 0
+    t_end = time.perf_counter() + args.clock_settle
+    while time.perf_counter() < t_end:
+        step(settle_calls)
+        settle_calls += 1
+        torch.cuda.synchronize()
+    print(f"[bench] clock settle {settle_calls} untimed calls; warmup {args.warmup} steps, kernel {kname}, "
+          f"{nsets} input set(s)", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # Kernel time on the launch stream.  A launch of the default workload
+    # takes milliseconds, and HIP events around each launch measure it
+    # directly.  A launch of the small workloads takes microseconds, of the
+    # order of an event pair's own cost, so those are timed as one event
+    # pair around the K back-to-back steps (the kernel trace of the same
+    # command gives the per-dispatch figure to compare with).
+    batch_timing = w.flops < 1e11
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
+    if batch_timing:
+        starts[0].record(stream)
+        for i in range(args.steps):
+            step(i)
+        ends[0].record(stream)
+    else:
+        for i in range(args.steps):
+            starts[i].record(stream)
+            step(i)
+            ends[i].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if batch_timing:
+        kernel_ms = [starts[0].elapsed_time(ends[0]) / args.steps]
+    else:
+        kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kernel_avg_ms = float(np.mean(kernel_ms))
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel "
           f"avg {kernel_avg_ms:.4f} ms (min {min(kernel_ms):.4f}, max {max(kernel_ms):.4f})",
@@ -510,6 +632,8 @@ def main():
     roof["algorithmic_flops_per_launch"] = flops_alg
     roof["algorithmic_bytes_per_launch"] = bytes_alg
     roof["kernel_avg_ms"] = kernel_avg_ms
+    roof["timing"] = ("one HIP event pair around the timed steps, back to back" if batch_timing
+                      else "HIP events around each timed launch")
     roof["kernel"] = kname
 
     result = {
@@ -519,6 +643,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"seconds": args.clock_settle, "untimed_calls": settle_calls},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -531,6 +656,14 @@ def main():
                    "input_scale": w.scale, "seed": w.seed, "input_sets": nsets},
         "roofline": roof,
     }
+    configs = []
+    if not args.no_configs:
+        for name in SMALL_CONFIGS:
+            if name != w.name:
+                configs.append(config_leg(torch, sdpa, inputs, name))
+        result["configs"] = {c["workload"]: {k: c[k] for k in ("us_per_call", "us_per_call_hot_cache", "value",
+                                                                "unit", "roofline", "kernel")}
+                             for c in configs}
     if not args.no_backward and w.dtype == "bf16":
         result["backward"] = backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args,
                                           flops_alg)
@@ -550,6 +683,18 @@ def main():
         lse_gpu = a[4].cpu().numpy()
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, kl, out_gpu, lse_gpu, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+    if args.all:
+        for c in configs:
+            line = {"metric": result["metric"], "value": c["value"], "unit": "TFLOP/s", "n_gpus": 1,
+                    "steps": c["calls_per_batch"], "warmup": 0, "ms_per_step": c["us_per_call"] * 1e-3,
+                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c["dtype"],
+                    "data": "synthetic",
+                    "config": {k: c[k] for k in ("workload", "B", "H", "Lq", "Lk", "d_k", "causal", "key_lens",
+                                                 "seed", "input_sets")},
+                    "roofline": c["roofline"], "kernel": c["kernel"],
+                    "us_per_call": c["us_per_call"], "us_per_call_hot_cache": c["us_per_call_hot_cache"],
+                    "us_per_call_batches": c["us_per_call_batches"]}
+            print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
