@@ -277,6 +277,30 @@ sdpa_status_t sdpa_decode(sdpa_handle_t h,
  */
 size_t sdpa_decode_workspace_size(sdpa_handle_t h, int B, int H, int Lq, int Lk, int d_k);
 
+/*
+ * sdpa_decode for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments, kernels and results as sdpa_decode, but the partial
+ * results of a split over keys go to a fixed device array that the library
+ * holds per GPU (SDPA_DECODE_NOALLOC_SCRATCH_BYTES, 16 MiB, kept until the
+ * process ends; its address is looked up when a bf16 handle is created on
+ * that device) instead of a caller workspace.  The call itself allocates
+ * nothing.  Every call on one GPU shares that array, so calls that overlap
+ * on one GPU (on different streams, or from several threads) race and must
+ * be serialised by the caller; the kernels write every partial result they
+ * read within the call, so nothing carries over from the previous call.
+ * Errors: as sdpa_decode, plus NOT_SUPPORTED when the split these sizes
+ * need is larger than the array (sdpa_decode_workspace_size(...) >
+ * SDPA_DECODE_NOALLOC_SCRATCH_BYTES) -- use sdpa_decode with a workspace
+ * then.
+ */
+#define SDPA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+sdpa_status_t sdpa_decode_noalloc(sdpa_handle_t h,
+                                  const void* q, const void* k, const void* v,
+                                  void* out, float* lse,
+                                  int B, int H, int Lq, int Lk, int d_k,
+                                  int causal, const int32_t* key_lens, void* stream);
+
 /* Release a handle (NULL is accepted).  Does not synchronise any stream. */
 sdpa_status_t sdpa_destroy(sdpa_handle_t h);
 

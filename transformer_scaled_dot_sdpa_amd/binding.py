@@ -22,8 +22,10 @@ DTYPE_FP32, DTYPE_BF16 = 0, 1
 
 # Every symbol include/sdpa.h declares.
 EXPORTED = ("sdpa_create", "sdpa_forward", "sdpa_forward_ex", "sdpa_backward", "sdpa_decode",
-            "sdpa_decode_workspace_size", "sdpa_destroy", "sdpa_status_string",
+            "sdpa_decode_workspace_size", "sdpa_decode_noalloc", "sdpa_destroy", "sdpa_status_string",
             "sdpa_kernel_name")
+# the fixed device array of sdpa_decode_noalloc (SDPA_DECODE_NOALLOC_SCRATCH_BYTES)
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class Layout(ctypes.Structure):
@@ -87,6 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.sdpa_backward.restype = i32
             lib.sdpa_decode.argtypes = [vp] * 6 + [i32] * 6 + [vp, vp, ctypes.c_size_t, vp]
             lib.sdpa_decode.restype = i32
+            lib.sdpa_decode_noalloc.argtypes = [vp] * 6 + [i32] * 6 + [vp, vp]
+            lib.sdpa_decode_noalloc.restype = i32
             lib.sdpa_decode_workspace_size.argtypes = [vp] + [i32] * 5
             lib.sdpa_decode_workspace_size.restype = ctypes.c_size_t
             lib.sdpa_destroy.argtypes = [vp]
@@ -143,6 +147,12 @@ def sdpa_decode(handle, q, k, v, out, lse, B, H, Lq, Lk, d_k, causal, key_lens, 
     return load_library().sdpa_decode(handle, q, k, v, out, lse, int(B), int(H), int(Lq), int(Lk),
                                       int(d_k), int(causal), key_lens, workspace,
                                       int(workspace_bytes), stream)
+
+
+def sdpa_decode_noalloc(handle, q, k, v, out, lse, B, H, Lq, Lk, d_k, causal, key_lens, stream) -> int:
+    """Raw ``sdpa_decode_noalloc`` on integer pointers; returns the status code."""
+    return load_library().sdpa_decode_noalloc(handle, q, k, v, out, lse, int(B), int(H), int(Lq), int(Lk),
+                                              int(d_k), int(causal), key_lens, stream)
 
 
 def sdpa_decode_workspace_size(handle, B, H, Lq, Lk, d_k) -> int:

@@ -110,6 +110,11 @@ sdpa_status_t sdpa_create(sdpa_handle_t* h, sdpa_dtype_t dtype, int device) {
         return SDPA_STATUS_HIP_ERROR;
     }
     if (dtype == SDPA_DTYPE_BF16 && !is_gfx950(prop.gcnArchName)) return SDPA_STATUS_NOT_SUPPORTED;
+    // address of the no-allocation decode scratch on this device (once per device)
+    if (dtype == SDPA_DTYPE_BF16 && sdpa::decode_scratch_init(device) != hipSuccess) {
+        (void)hipGetLastError();
+        return SDPA_STATUS_HIP_ERROR;
+    }
     sdpa_ctx* c = new (std::nothrow) sdpa_ctx;
     if (c == nullptr) return SDPA_STATUS_ALLOC_FAILED;
     c->dtype = dtype;
@@ -398,10 +403,17 @@ size_t sdpa_decode_workspace_size(sdpa_handle_t h, int B, int H, int Lq, int Lk,
     return sdpa::plan_decode(B, H, Lq, Lk, d_k, h->num_cus).workspace_bytes;
 }
 
-sdpa_status_t sdpa_decode(sdpa_handle_t h, const void* q, const void* k, const void* v, void* out,
+}  // extern "C"
+
+namespace {
+
+// sdpa_decode and sdpa_decode_noalloc: validation and launch.  noalloc: the
+// partial results go to the library's own scratch array instead of a
+// caller workspace.
+sdpa_status_t decode_impl(sdpa_handle_t h, const void* q, const void* k, const void* v, void* out,
                           float* lse, int B, int H, int Lq, int Lk, int d_k, int causal,
                           const int32_t* key_lens, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          bool noalloc, void* stream) {
     if (h == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr)
         return SDPA_STATUS_INVALID_VALUE;
     if (B < 1 || H < 1 || Lq < 1 || Lk < 1 || d_k < 1) return SDPA_STATUS_INVALID_VALUE;
@@ -415,14 +427,21 @@ sdpa_status_t sdpa_decode(sdpa_handle_t h, const void* q, const void* k, const v
     const size_t bq = (size_t)nq * 2, bkv = (size_t)nkv * 2;
     const size_t bl = (size_t)B * H * Lq * sizeof(float);
     const sdpa::DecodePlan plan = sdpa::plan_decode(B, H, Lq, Lk, d_k, h->num_cus);
-    if (plan.workspace_bytes > 0) {
+    if (noalloc) {
+        if (plan.workspace_bytes > sdpa::kDecodeNoallocScratchBytes) return SDPA_STATUS_NOT_SUPPORTED;
+        workspace = plan.workspace_bytes > 0 ? sdpa::decode_scratch_ptr(h->device) : nullptr;
+        if (plan.workspace_bytes > 0 && workspace == nullptr) return SDPA_STATUS_HIP_ERROR;
+        workspace_bytes = plan.workspace_bytes;
+    } else if (plan.workspace_bytes > 0) {
         if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return SDPA_STATUS_INVALID_VALUE;
         if (reinterpret_cast<uintptr_t>(workspace) % alignof(float) != 0) return SDPA_STATUS_INVALID_VALUE;
     }
     struct Span { const void* p; size_t n; };
     const Span inputs[] = {{q, bq}, {k, bkv}, {v, bkv}};
+    // (the library's own scratch is an allocation of its own: it cannot
+    // overlap caller memory)
     const Span outputs[] = {{out, bq}, {lse, lse ? bl : 0},
-                            {workspace, plan.workspace_bytes}};
+                            {workspace, noalloc ? 0 : plan.workspace_bytes}};
     for (size_t o = 0; o < 3; ++o) {
         if (outputs[o].p == nullptr || outputs[o].n == 0) continue;
         for (const Span& in : inputs)
@@ -457,6 +476,25 @@ sdpa_status_t sdpa_decode(sdpa_handle_t h, const void* q, const void* k, const v
     hipError_t e = sdpa::launch_decode_bf16(a, plan, static_cast<hipStream_t>(stream));
     if (cur != h->device) (void)hipSetDevice(cur);
     return e == hipSuccess ? SDPA_STATUS_SUCCESS : SDPA_STATUS_HIP_ERROR;
+}
+
+}  // namespace
+
+extern "C" {
+
+sdpa_status_t sdpa_decode(sdpa_handle_t h, const void* q, const void* k, const void* v, void* out,
+                          float* lse, int B, int H, int Lq, int Lk, int d_k, int causal,
+                          const int32_t* key_lens, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    return decode_impl(h, q, k, v, out, lse, B, H, Lq, Lk, d_k, causal, key_lens, workspace,
+                       workspace_bytes, false, stream);
+}
+
+sdpa_status_t sdpa_decode_noalloc(sdpa_handle_t h, const void* q, const void* k, const void* v,
+                                  void* out, float* lse, int B, int H, int Lq, int Lk, int d_k,
+                                  int causal, const int32_t* key_lens, void* stream) {
+    return decode_impl(h, q, k, v, out, lse, B, H, Lq, Lk, d_k, causal, key_lens, nullptr, 0, true,
+                       stream);
 }
 
 }  // extern "C"

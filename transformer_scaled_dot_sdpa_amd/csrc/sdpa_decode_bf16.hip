@@ -27,8 +27,24 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace sdpa {
+
+// Device memory of sdpa_decode_noalloc: the per-chunk partial results live
+// here instead of in a caller workspace.  One copy per GPU, held until the
+// process ends; every call on a GPU shares it (calls that overlap on one GPU
+// race).  The kernels write every partial they read in the same call, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[kDecodeNoallocScratchBytes];
+
 namespace {
+
+// Device address of `scratch` per device ordinal, looked up once per device
+// (in host code the array's name is only a stand-in for the symbol).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -368,6 +384,28 @@ DecodePlan plan_decode(int B, int H, int Lq, int Lk, int d, int num_cus) {
     const long long rows = (long long)B * H * Lq;
     plan.workspace_bytes = splits > 1 ? (size_t)splits * rows * (size_t)(d + 1) * sizeof(float) : 0;
     return plan;
+}
+
+hipError_t decode_scratch_init(int device) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device] != nullptr) return hipSuccess;
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = ptr;
+    return hipSuccess;
+}
+
+void* decode_scratch_ptr(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[device];
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s) {

@@ -124,6 +124,14 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s);
+
+// The library's own decode scratch (sdpa_decode_noalloc): a fixed-size
+// device array per GPU.  decode_scratch_init looks up its address on one
+// device (once; later calls return at once) and must run before
+// decode_scratch_ptr can return it; nullptr before that.
+constexpr size_t kDecodeNoallocScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch_init(int device);
+void* decode_scratch_ptr(int device);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
 
 }  // namespace sdpa
