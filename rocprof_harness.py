@@ -26,8 +26,10 @@ not being profiled switched off:
   scale factor to bytes (``calibration_factor``), so that HBM bytes per
   launch = counter KiB * 1024 * factor.
 
-Raw rocprofv3 output stays under ``--raw`` (default ``gpurun_out/rocprof``);
-only the summaries go to ``--out`` (default ``profiles/``).  The forward
+Raw rocprofv3 output (CSV files, tens of MB for a trace) goes to ``--raw``
+(default: a fresh directory under the system temp directory) and is not
+kept; only the summaries go to ``--out`` (default ``profiles/``).  The fp32
+workloads get no MFMA pass (their kernel uses no matrix cores).  The forward
 traffic summary carries ``kernel_source_sha256`` and
 ``traffic_bytes_per_launch`` lines, which bench.py reads for its roofline.
 """
@@ -41,6 +43,7 @@ import re
 import shlex
 import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -74,12 +77,10 @@ def bench_args(workload: str, leg: str, steps: int, warmup: int, extra=()) -> li
 def pass_command(kind: str, workload: str, leg: str, raw: str, steps: int, warmup: int) -> tuple[list[str], str]:
     """(argv, output directory) of one rocprofv3 pass."""
     tag = f"{kind}_{leg}_{workload}"
-    # relative to the repository root (the passes run there), so that the
-    # summaries carry commands that run on any copy of the repository
-    out = os.path.relpath(os.path.join(raw, tag), ROOT)
+    out = os.path.join(raw, tag)
     if kind == "trace":
         prof = ["--kernel-trace", "--stats"]
-        b = bench_args(workload, leg, steps, warmup)
+        b = bench_args(workload, leg, steps, warmup, ["--clock-settle", "0.1"])
     elif kind == "mfma":
         prof = ["--pmc", *MFMA_COUNTERS]
         b = bench_args(workload, leg, 3, 1, ["--clock-settle", "0.05"])
@@ -174,12 +175,24 @@ def run_pass(argv: list[str], log: str, timeout: int) -> str:
     # rocprofv3 can end with a segmentation fault after the program finished
     # and its files are complete; the bench line printed is the check
     if bench_json(r.stdout) is None:
-        raise RuntimeError(f"pass failed (rc {r.returncode}); see {log}")
+        tail = open(log, errors="replace").read().splitlines()[-30:]
+        print("\n".join(["[harness] last lines of the pass's log:"] + tail), flush=True)
+        raise RuntimeError(f"pass failed (rc {r.returncode}); log {log}")
     return r.stdout
 
 
+_RAW_SHOWN = "$RAW"
+
+
 def cmd_str(argv: list[str]) -> str:
-    return " ".join(shlex.quote(a) for a in argv)
+    """The command as run, with the raw-output directory shown as $RAW (a
+    temporary directory of the run)."""
+    out = []
+    for i, a in enumerate(argv):
+        if i > 0 and argv[i - 1] == "-d":
+            a = os.path.join(_RAW_SHOWN, os.path.basename(a))
+        out.append(a if a.startswith("$RAW") else shlex.quote(a))
+    return " ".join(out)
 
 
 def kernel_source_hash() -> str:
@@ -327,7 +340,7 @@ def main():
     ap.add_argument("--workload", action="append", default=None)
     ap.add_argument("--leg", default="forward", choices=list(LEG_KERNELS))
     ap.add_argument("--passes", default="trace,mfma,fetch,write")
-    ap.add_argument("--raw", default=os.path.join("gpurun_out", "rocprof"))
+    ap.add_argument("--raw", default=None, help="directory for rocprofv3's raw output (default: a temp dir)")
     ap.add_argument("--out", default="profiles")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
@@ -337,8 +350,11 @@ def main():
     workloads = args.workload or ["large_causal_d128"]
     passes = args.passes.split(",")
     os.chdir(ROOT)
+    if args.raw is None:
+        args.raw = tempfile.mkdtemp(prefix="rocprof_harness_")
     os.makedirs(args.raw, exist_ok=True)
     os.makedirs(args.out, exist_ok=True)
+    print(f"[harness] raw output under {args.raw}", flush=True)
     for wl in workloads:
         cmds, raws = {}, {}
         for kind in passes:
@@ -351,7 +367,8 @@ def main():
         if "trace" in passes:
             out = run_pass(cmds["trace"], raws["trace"] + ".log", args.timeout)
             trace_avg, js = write_trace(args.out, wl, args.leg, cmds["trace"], raws["trace"], out, args.steps)
-        if "mfma" in passes:
+        fp32 = wl.startswith("toy")
+        if "mfma" in passes and not fp32:
             run_pass(cmds["mfma"], raws["mfma"] + ".log", args.timeout)
             write_mfma(args.out, wl, args.leg, cmds["mfma"], raws["mfma"], trace_avg)
         if "fetch" in passes and "write" in passes:
