@@ -24,9 +24,10 @@ in HBM.  W untimed steps, then K timed steps bracketed by
   from dout, out and lse), timed the same way after the forward steps; its
   algorithmic work is 10*d_k flops per valid pair (five products of 2*d_k:
   S and dP recomputed once, dV, dQ, dK), reported against the same peak;
-* ``decode``: ``sdpa_decode`` (1..8 query rows, split over key chunks) on a
-  decode-shaped workload (default ``decode_d128``), timed with HIP events,
-  reported as HBM GB/s of algorithmic bytes (the workload is bandwidth
+* ``decode``: ``sdpa_decode`` (1..8 query rows, split over key chunks) on the
+  decode-shaped workloads (default ``decode_d128`` and ``decode_d64_single``),
+  each timed as batches of back-to-back calls between two HIP events,
+  reported as HBM GB/s of algorithmic bytes (the workloads are bandwidth
   bound), with ``sdpa_forward`` timed on the same inputs beside it;
 * ``forward_ex``: ``sdpa_forward_ex`` on the main workload's own inputs in
   the head-interleaved [B, L, H*d] layout, and with an additive fp32 bias
@@ -364,7 +365,7 @@ def decode_leg(torch, sdpa, inputs, name, args):
     tkl = torch.from_numpy(kl).cuda() if kl is not None else None
     _, bytes_alg = algorithmic_work(w, kl)
     set_bytes = (tq.numel() + tk.numel() + tv.numel()) * 2
-    nsets = 1 if set_bytes >= (1 << 30) else int(math.ceil((1 << 30) / set_bytes))
+    nsets = 1 if set_bytes >= (1 << 30) else min(64, int(math.ceil((1 << 30) / set_bytes)))
     sets = [(tq, tk, tv)] + [(tq.clone(), tk.clone(), tv.clone()) for _ in range(nsets - 1)]
     out = torch.empty_like(tq)
     lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
@@ -383,16 +384,22 @@ def decode_leg(torch, sdpa, inputs, name, args):
                 fn(sets[i % nsets])
                 i += 1
             torch.cuda.synchronize()
-        st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        for i in range(steps):
-            st[i].record(stream)
-            fn(sets[i % nsets])
-            en[i].record(stream)
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in zip(st, en)]))
+        # one event pair around the back-to-back calls (a call can take a
+        # few microseconds, of the order of an event pair's own cost);
+        # median of 3 batches
+        res = []
+        for _ in range(3):
+            st = torch.cuda.Event(enable_timing=True)
+            en = torch.cuda.Event(enable_timing=True)
+            st.record(stream)
+            for i in range(steps):
+                fn(sets[i % nsets])
+            en.record(stream)
+            torch.cuda.synchronize()
+            res.append(st.elapsed_time(en) / steps)
+        return float(np.median(res))
 
-    steps = max(1, min(args.steps, 50))
+    steps = 200 if w.B * w.H * w.Lk < (1 << 24) else 50
     dec_ms = timed(lambda a: sdpa.decode(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=out,
                                          lse=lse, workspace=ws, stream=stream), steps)
     fwd_ms = timed(lambda a: sdpa.forward(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=out,
@@ -446,7 +453,7 @@ def config_leg(torch, sdpa, inputs, name, batch=200, batches=5):
     tkl = torch.from_numpy(kl).cuda() if kl is not None else None
     flops_alg, bytes_alg = algorithmic_work(w, kl)
     per_set = sum(t.numel() * t.element_size() for t in base) * 2 + w.B * w.H * w.Lq * 4
-    nsets = max(8, int(math.ceil((300 << 20) / per_set)))
+    nsets = min(64, max(8, int(math.ceil((300 << 20) / per_set))))
     sets = [tuple(t.clone() for t in base) + (torch.empty_like(base[0]),
                                                torch.empty((w.B, w.H, w.Lq), dtype=torch.float32,
                                                            device="cuda")) for _ in range(nsets)]
@@ -509,8 +516,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
-    ap.add_argument("--decode-workload", default="decode_d128",
-                    help="decode-shaped workload of the decode leg ('none' skips it)")
+    ap.add_argument("--decode-workload", default="decode_d128,decode_d64_single",
+                    help="decode-shaped workloads of the decode leg, comma-separated ('none' skips it)")
     ap.add_argument("--no-forward-ex", action="store_true", help="skip the forward_ex leg")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip the vendor GEMM context measurement")
@@ -555,7 +562,9 @@ def main():
     # Small workloads fit in the 256 MB Infinity Cache: rotate several input
     # copies so every step reads HBM.
     set_bytes = (tq.numel() + tk.numel() + tv.numel()) * tq.element_size() * 2
-    nsets = 1 if set_bytes >= (1 << 30) else int(math.ceil((1 << 30) / set_bytes))
+    # (at most 64: a problem too small to need that many is bound by launch
+    # latency, not by HBM)
+    nsets = 1 if set_bytes >= (1 << 30) else min(64, int(math.ceil((1 << 30) / set_bytes)))
     sets = [(tq, tk, tv, torch.empty_like(tq),
              torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda"))]
     for _ in range(nsets - 1):
@@ -670,7 +679,8 @@ def main():
     if not args.no_forward_ex and w.dtype == "bf16":
         result["forward_ex"] = forward_ex_leg(torch, sdpa, w, sets, tkl, stream, args)
     if args.decode_workload != "none":
-        result["decode"] = decode_leg(torch, sdpa, inputs, args.decode_workload, args)
+        result["decode"] = {name: decode_leg(torch, sdpa, inputs, name, args)
+                            for name in args.decode_workload.split(",")}
     if not args.no_vendor_gemm:
         g = vendor_gemm(torch)
         g["attention_value_over_gemm"] = value / g["value"]

@@ -137,7 +137,7 @@ typedef struct {
  *                -inf gets out = 0 and lse = -inf.
  * causal and key_lens apply as in sdpa_forward, on top of the mask.
  *   tile         NULL for the configuration sdpa_forward would choose, or the
- *                name of a compiled one ("bf16_d64_bc64_w4_ks2", ...; fp32:
+ *                name of a compiled one ("bf16_d128_bc64_w4_ks2", ...; fp32:
  *                "f32_wave_per_row").  Every configuration computes the same
  *                function; they differ in speed.  d_v != d_k and a mask run
  *                only in the default bf16 configuration of each d_k

@@ -235,10 +235,11 @@ def write_trace(out_dir, workload, leg, argv, raw, stdout, steps):
             lines += ["", f"Same command, HIP events inside bench.py: {js['backward']['ms_per_call'] * 1e6:.0f} ns "
                           f"per backward call ({js['backward']['roofline']['achieved']:.1f} TFLOP/s at 10*d_k "
                           "flops per valid pair)."]
-        elif leg == "decode" and "decode" in js:
-            d = js["decode"]
-            lines += ["", f"Same command, HIP events inside bench.py: {d['us_per_call']:.1f} us per decode call "
-                          f"({d['roofline']['achieved']:.0f} GB/s of algorithmic bytes)."]
+        elif leg == "decode" and workload in js.get("decode", {}):
+            d = js["decode"][workload]
+            lines += ["", f"Same command, bench.py's own timing (one HIP event pair around {d['steps']} back-to-back "
+                          f"calls): {d['us_per_call']:.1f} us per decode call ({d['roofline']['achieved']:.0f} GB/s "
+                          "of algorithmic bytes)."]
         elif leg == "forward_ex" and "forward_ex" in js:
             f = js["forward_ex"]
             lines += ["", "Same command, HIP events inside bench.py: " + ", ".join(
@@ -377,8 +378,8 @@ def main():
             jsb = bench_json(out)
             alg = None
             if jsb is not None:
-                if args.leg == "decode" and "decode" in jsb:
-                    alg = jsb["decode"]["roofline"]["algorithmic_bytes_per_call"]
+                if args.leg == "decode" and wl in jsb.get("decode", {}):
+                    alg = jsb["decode"][wl]["roofline"]["algorithmic_bytes_per_call"]
                 elif args.leg in ("forward", "forward_ex"):
                     alg = jsb["roofline"].get("algorithmic_bytes_per_launch")
             write_traffic(args.out, wl, args.leg, cmds, raws, alg)
