@@ -400,13 +400,23 @@ def decode_leg(torch, sdpa, inputs, name, args):
         return float(np.median(res))
 
     steps = 200 if w.B * w.H * w.Lk < (1 << 24) else 50
-    dec_ms = timed(lambda a: sdpa.decode(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=out,
-                                         lse=lse, workspace=ws, stream=stream), steps)
-    fwd_ms = timed(lambda a: sdpa.forward(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=out,
-                                          lse=lse, stream=stream), steps)
+    dec = lambda a, st=stream: sdpa.decode(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=out, lse=lse,
+                                           workspace=ws, stream=st)
+    fwd = lambda a, st=stream: sdpa.forward(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=out, lse=lse,
+                                            stream=st)
+    dec_eager_ms = timed(dec, steps)
+    # the GPU's time per call: the same calls replayed from a HIP graph
+    dec_us, _ = graph_replay_us(torch, [lambda a=sets[i % nsets]: dec(a, None) for i in range(steps)], [out, lse])
+    dec_ms = dec_us * 1e-3
+    fwd_ms = None
+    if not args.no_decode_forward:
+        fwd_us, _ = graph_replay_us(torch, [lambda a=sets[i % nsets]: fwd(a, None) for i in range(steps)],
+                                    [out, lse])
+        fwd_ms = fwd_us * 1e-3
     gbs = bytes_alg / (dec_ms * 1e-3) / 1e9
-    print(f"[bench] decode {w.name}: {dec_ms*1e3:.1f} us ({gbs:.0f} GB/s); forward on the same "
-          f"inputs {fwd_ms*1e3:.1f} us", file=sys.stderr, flush=True)
+    print(f"[bench] decode {w.name}: {dec_ms*1e3:.1f} us ({gbs:.0f} GB/s; eager launches {dec_eager_ms*1e3:.1f} us)"
+          + (f"; forward on the same inputs {fwd_ms*1e3:.1f} us" if fwd_ms is not None else ""),
+          file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -424,14 +434,55 @@ def decode_leg(torch, sdpa, inputs, name, args):
     res = {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d_k": w.d,
             "key_lens": None if kl is None else "uniform[%d,%d]" % w.key_lens,
             "input_sets": nsets, "steps": steps, "us_per_call": dec_ms * 1e3,
+            "timing": "one HIP event pair around a HIP graph of the back-to-back calls, median of 5 replays",
+            "us_per_call_eager": dec_eager_ms * 1e3,
             "workspace_bytes": need,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_call": bytes_alg,
                          "kernels": "the forward kernel when the slices fill the GPU (decode_d128), else decode_kernel (+ decode_combine when split)"},
-            "forward_same_inputs_us": fwd_ms * 1e3}
+            "forward_same_inputs_us": fwd_ms * 1e3 if fwd_ms is not None else None}
     if cpu is not None:
         res["cpu_baseline"] = cpu
     return res
+
+
+def graph_replay_us(torch, calls, outputs, reps=5):
+    """Per-call GPU time of `calls` (functions that each enqueue one library
+    call on the current stream) captured into one HIP graph and replayed
+    `reps` times; median over the replays.  A short call takes a few
+    microseconds, about what the Python binding needs to enqueue one, so
+    eager back-to-back calls measure the host's launch rate; the graph
+    replays the same kernels without it.  `outputs` (tensors the calls
+    write) are compared bit for bit with the eager results after the first
+    and the last replay (the outputs of deterministic kernels on the same
+    inputs)."""
+    import numpy as np
+    for c in calls:                       # eager reference (and warm-up)
+        c()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    res = []
+    for r in range(reps):
+        for t in outputs:
+            t.fill_(float("nan") if t.is_floating_point() else 0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1e3 / len(calls))
+        if r in (0, reps - 1):
+            for t, rt in zip(outputs, ref):
+                if not torch.equal(t.view(torch.uint8), rt.view(torch.uint8)):
+                    raise RuntimeError("graph replay differs from the eager calls")
+    del g
+    return float(np.median(res)), res
 
 
 SMALL_CONFIGS = ["toy_f32", "encoder_d64", "decoder_causal_d64", "cross_padded_d64"]
@@ -459,7 +510,7 @@ def config_leg(torch, sdpa, inputs, name, batch=200, batches=5):
                                                            device="cuda")) for _ in range(nsets)]
     stream = torch.cuda.current_stream()
 
-    def call(a):
+    def call(a, stream=stream):
         sdpa.forward(a[0], a[1], a[2], causal=w.causal, key_lens=tkl, out=a[3], lse=a[4], stream=stream)
 
     t_end = time.perf_counter() + 0.2
@@ -483,13 +534,21 @@ def config_leg(torch, sdpa, inputs, name, batch=200, batches=5):
             res.append(e0.elapsed_time(e1) * 1e3 / batch)
         return float(np.median(res)), res
 
-    us, all_us = timed(True)
-    us_hot, _ = timed(False)
+    us_eager, eager_all = timed(True)
+    us_eager_hot, _ = timed(False)
+    # the same calls replayed from a HIP graph (the GPU's time per call)
+    outs = [x for a in sets for x in a[3:5]]
+    us, all_us = graph_replay_us(torch, [lambda a=sets[j % nsets]: call(a, None) for j in range(batch)], outs)
+    us_hot, _ = graph_replay_us(torch, [lambda: call(sets[0], None) for _ in range(batch)], list(sets[0][3:5]))
     gbs = bytes_alg / (us * 1e-6) / 1e9
     out = {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d_k": w.d, "dtype": w.dtype,
            "causal": w.causal, "key_lens": None if kl is None else "uniform[%d,%d]" % w.key_lens,
            "seed": w.seed, "kernel": sdpa.kernel_name(base[0], base[1], w.causal, kl is not None),
+           "timing": ("one HIP event pair around a HIP graph of the back-to-back calls (rotated input "
+                      "sets), median of 5 replays; eager: the same calls launched from Python"),
            "us_per_call": us, "us_per_call_batches": all_us, "us_per_call_hot_cache": us_hot,
+           "us_per_call_eager": us_eager, "us_per_call_eager_batches": eager_all,
+           "us_per_call_eager_hot_cache": us_eager_hot,
            "calls_per_batch": batch, "input_sets": nsets,
            "value": w.flops / (us * 1e-6) / 1e12, "unit": "TFLOP/s",
            "algorithmic_flops_per_call": flops_alg, "algorithmic_bytes_per_call": bytes_alg}
@@ -499,8 +558,8 @@ def config_leg(torch, sdpa, inputs, name, batch=200, batches=5):
     else:
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": gbs / PEAK_HBM_GBS}
-    print(f"[bench] config {w.name}: {us:.2f} us/call rotated, {us_hot:.2f} us hot, {gbs:.0f} GB/s, "
-          f"kernel {out['kernel']}", file=sys.stderr, flush=True)
+    print(f"[bench] config {w.name}: {us:.2f} us/call rotated (graph; eager {us_eager:.2f}), {us_hot:.2f} us hot, "
+          f"{gbs:.0f} GB/s, kernel {out['kernel']}", file=sys.stderr, flush=True)
     del sets, base
     return out
 
@@ -519,6 +578,8 @@ def main():
     ap.add_argument("--decode-workload", default="decode_d128,decode_d64_single",
                     help="decode-shaped workloads of the decode leg, comma-separated ('none' skips it)")
     ap.add_argument("--no-forward-ex", action="store_true", help="skip the forward_ex leg")
+    ap.add_argument("--no-decode-forward", action="store_true",
+                    help="in the decode leg, skip timing sdpa_forward on the same inputs")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip the vendor GEMM context measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -597,9 +658,10 @@ def main():
     # Kernel time on the launch stream.  A launch of the default workload
     # takes milliseconds, and HIP events around each launch measure it
     # directly.  A launch of the small workloads takes microseconds, of the
-    # order of an event pair's own cost, so those are timed as one event
-    # pair around the K back-to-back steps (the kernel trace of the same
-    # command gives the per-dispatch figure to compare with).
+    # order of an event pair's own cost and of the binding's launch cost, so
+    # those are timed as the K steps replayed from a HIP graph (the kernel
+    # trace of the same command gives the per-dispatch figure to compare
+    # with).
     batch_timing = w.flops < 1e11
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -619,7 +681,13 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     if batch_timing:
-        kernel_ms = [starts[0].elapsed_time(ends[0]) / args.steps]
+        # the GPU's time per step: the same K steps replayed from a HIP graph
+        # (eager launches from Python would measure the host's launch rate)
+        us, _ = graph_replay_us(torch, [lambda i=i: sdpa.forward(
+            sets[i % nsets][0], sets[i % nsets][1], sets[i % nsets][2], causal=w.causal, key_lens=tkl,
+            out=sets[i % nsets][3], lse=sets[i % nsets][4]) for i in range(args.steps)],
+            [x for a in sets for x in a[3:5]])
+        kernel_ms = [us * 1e-3]
     else:
         kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kernel_avg_ms = float(np.mean(kernel_ms))
@@ -641,7 +709,7 @@ def main():
     roof["algorithmic_flops_per_launch"] = flops_alg
     roof["algorithmic_bytes_per_launch"] = bytes_alg
     roof["kernel_avg_ms"] = kernel_avg_ms
-    roof["timing"] = ("one HIP event pair around the timed steps, back to back" if batch_timing
+    roof["timing"] = ("one HIP event pair around a HIP graph of the K steps, median of 5 replays" if batch_timing
                       else "HIP events around each timed launch")
     roof["kernel"] = kname
 
@@ -670,8 +738,9 @@ def main():
         for name in SMALL_CONFIGS:
             if name != w.name:
                 configs.append(config_leg(torch, sdpa, inputs, name))
-        result["configs"] = {c["workload"]: {k: c[k] for k in ("us_per_call", "us_per_call_hot_cache", "value",
-                                                                "unit", "roofline", "kernel")}
+        result["configs"] = {c["workload"]: {k: c[k] for k in ("us_per_call", "us_per_call_hot_cache",
+                                                                "us_per_call_eager", "value", "unit", "roofline",
+                                                                "kernel")}
                              for c in configs}
     if not args.no_backward and w.dtype == "bf16":
         result["backward"] = backward_leg(torch, sdpa, inputs, w, sets, tkl, stream, args,

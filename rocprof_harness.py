@@ -64,7 +64,7 @@ def bench_args(workload: str, leg: str, steps: int, warmup: int, extra=()) -> li
     if leg == "decode":
         # the decode leg runs after a minimal main leg on the smallest workload
         a += ["--workload", "toy_f32", "--decode-workload", workload, "--no-backward", "--no-forward-ex",
-              "--clock-settle", "0"]
+              "--no-decode-forward"]
     else:
         a += ["--workload", workload, "--decode-workload", "none"]
         if leg != "backward":
@@ -237,9 +237,9 @@ def write_trace(out_dir, workload, leg, argv, raw, stdout, steps):
                           "flops per valid pair)."]
         elif leg == "decode" and workload in js.get("decode", {}):
             d = js["decode"][workload]
-            lines += ["", f"Same command, bench.py's own timing (one HIP event pair around {d['steps']} back-to-back "
-                          f"calls): {d['us_per_call']:.1f} us per decode call ({d['roofline']['achieved']:.0f} GB/s "
-                          "of algorithmic bytes)."]
+            lines += ["", f"Same command, bench.py's own timing ({d.get('timing', 'HIP events')}, "
+                          f"{d['steps']} calls): {d['us_per_call']:.1f} us per decode call "
+                          f"({d['roofline']['achieved']:.0f} GB/s of algorithmic bytes)."]
         elif leg == "forward_ex" and "forward_ex" in js:
             f = js["forward_ex"]
             lines += ["", "Same command, HIP events inside bench.py: " + ", ".join(
