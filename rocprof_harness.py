@@ -244,7 +244,10 @@ def write_trace(out_dir, workload, leg, argv, raw, stdout, steps):
             f = js["forward_ex"]
             lines += ["", "Same command, HIP events inside bench.py: " + ", ".join(
                 f"{k} {v['us_per_call']:.1f} us" for k, v in f.items() if isinstance(v, dict))]
-    lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    lines += ["", "bench.py's own figure comes from the same profiled run; the kernel trace adds work per "
+                  "dispatch, which matters for calls of a few microseconds (there the unprofiled bench.py line is "
+                  "the one to quote) and not for kernels of a millisecond.",
+              "", f"kernel_source_sha256: {kernel_source_hash()}", ""]
     name = {"forward": "kernel_stats", "backward": "backward_trace", "decode": "decode_trace",
             "forward_ex": "forward_ex"}[leg]
     path = os.path.join(out_dir, f"{workload}_{name}.md")

@@ -128,6 +128,9 @@ CASES = [
     (1, 2, 100, 333, True, None),
     (2, 1, 520, 520, True, [300, 520]),
     (1, 1, 256, 64, False, None),
+    # causal, an even number of blocks per slice, between one and two blocks
+    # per compute unit: the kernels renumber their units in compute-unit pairs
+    (2, 80, 256, 256, True, None),
 ]
 
 

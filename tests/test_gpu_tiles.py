@@ -39,6 +39,14 @@ CASES = [
     # pairs tiles rank batches by length and run the middle item alone)
     (5, 3, 200, 300, False, [300, 17, 300, 0, 150]),
     (3, 1, 100, 200, False, [5, 200, 100]),
+    # causal, an even number of query blocks per slice and between one and
+    # two blocks per compute unit: the default tile's compute-unit pairing
+    # renumbers the units
+    (2, 80, 256, 256, True, None),
+    # key lengths, no causal mask, between one and two blocks per compute
+    # unit, 5 key tiles: the default tile orders items by length rank
+    # interleaved from both ends and pairs them per compute unit
+    (8, 40, 100, 300, False, [300, 5, 0, 150, 299, 64, 1, 200]),
 ]
 
 

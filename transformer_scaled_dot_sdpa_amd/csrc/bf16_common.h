@@ -42,6 +42,11 @@ struct KParams {
     // key-length pairs (LENS kernels): batches ordered by clamped key length,
     // longest first, and unit u runs items u and num_items - 1 - u
     int lens_pairs;
+    // one unit per workgroup, all resident at once, units alternating long
+    // and short (causal): renumber so that the two workgroups a compute unit
+    // holds take a long unit and the short one beside it (cu_pairs = compute
+    // units per XCD; 0: off)
+    int cu_pairs;
     float scale_log2;  // log2(e) * scale (scale = 1 / sqrt(d) unless given)
     // Element strides of the [B, H, L, width] views: batch, head, row.
     long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
@@ -151,6 +156,30 @@ __device__ __forceinline__ void workgroup_units(int num_units, int* first, int* 
     *first = ulo + j;
     *step = sx;
     *last = uhi;
+}
+
+// With one unit per workgroup and every workgroup resident at once, the
+// hardware hands an XCD's workgroups to its C compute units in turn, so the
+// XCD's j-th and (j + C)-th workgroups share a compute unit.  Units that
+// alternate long and short (causal query blocks) would then put two long
+// ones on every other compute unit.  This renumbering gives local workgroup
+// j < P the unit 2j and workgroup j + C the unit 2j + 1 (P = R - C pairs of an
+// XCD range of R units), so that each compute unit holding two workgroups
+// runs one long and one short unit -- of the same head, which also shares
+// its K/V in L2.  unit_first is the workgroup's unit from workgroup_units.
+__device__ __forceinline__ int cu_pair_unit(int num_units, int cus_per_xcd, int unit_first) {
+    const int nwg = gridDim.x;
+    const int g = blockIdx.x;
+    const int xcd = g & 7, j = g >> 3;
+    const int per = nwg >> 3, rem = nwg & 7;
+    const int sx = per + (xcd < rem ? 1 : 0);
+    const int wlo = xcd * per + (xcd < rem ? xcd : rem);
+    const int ulo = (int)((long long)num_units * wlo / nwg);
+    const int R = sx, C = cus_per_xcd;
+    if (num_units != nwg || R <= C || R > 2 * C || (ulo & 1)) return unit_first;
+    const int P = R - C;
+    const int local = j < P ? 2 * j : (j >= C ? 2 * (j - C) + 1 : 2 * P + (j - P));
+    return ulo + local;
 }
 
 // Work item -> (b*H + h, query block).  Causal query blocks of a head are

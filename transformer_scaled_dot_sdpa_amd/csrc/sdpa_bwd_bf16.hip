@@ -57,6 +57,7 @@ struct BParams {
     int num_items;
     int upi;
     int num_units;
+    int cu_pairs;      // compute units per XCD when units are renumbered in compute-unit pairs, else 0
     float scale;       // 1 / sqrt(d)
     float scale_log2;  // log2(e) / sqrt(d)
 };
@@ -161,6 +162,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BParams p) {
 
     int unit_first, unit_step, unit_last;
     workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
+    if (CAUSAL && p.cu_pairs > 0) unit_first = cu_pair_unit(p.num_units, p.cu_pairs, unit_first);
     for (int unit = unit_first; unit < unit_last; unit += unit_step)
     for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
     int bh, qb;
@@ -346,6 +348,7 @@ __global__ void __launch_bounds__(256, MODE == 0 ? 1 : 2) bwd_dkdv_kernel(BParam
 
     int unit_first, unit_step, unit_last;
     workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
+    if (CAUSAL && p.cu_pairs > 0) unit_first = cu_pair_unit(p.num_units, p.cu_pairs, unit_first);
     for (int unit = unit_first; unit < unit_last; unit += unit_step)
     for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
     int bh, kb;
@@ -598,8 +601,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
 
     // causal work runs as long/short pairs of items once the items
     // outnumber the resident workgroups (2 per CU); a smaller problem takes
-    // one item per workgroup so that every item starts at once
-    const long long slots = (long long)(a.num_cus > 0 ? a.num_cus : 256) * 2;
+    // one item per workgroup so that every item starts at once, renumbered
+    // so that a compute unit holding two runs a long and a short one
+    // (cu_pair_unit; the query or key blocks of a slice alternate long and
+    // short, and an even count keeps the alternation aligned)
+    const int cus = a.num_cus > 0 ? a.num_cus : 256;
+    const long long slots = (long long)cus * 2;
+    auto cu_pairs_for = [&](long long items) {
+        return (CAUSAL && p.upi == 1 && items <= slots && items > cus && p.num_blocks % 2 == 0 && cus % 8 == 0)
+                   ? cus / 8 : 0;
+    };
     {
         p.num_blocks = (a.Lq + 127) / 128;
         const long long items = (long long)p.num_blocks * a.B * a.H;
@@ -607,6 +618,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         p.num_items = (int)items;
         p.upi = (CAUSAL && items > slots) ? 2 : 1;
         p.num_units = (int)((items + p.upi - 1) / p.upi);
+        p.cu_pairs = cu_pairs_for(items);
         hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, LENS>), dim3((unsigned)p.num_units), dim3(256), 0,
                            stream, p);
         hipError_t e = hipGetLastError();
@@ -619,6 +631,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         p.num_items = (int)items;
         p.upi = (CAUSAL && items > slots) ? 2 : 1;
         p.num_units = (int)((items + p.upi - 1) / p.upi);
+        p.cu_pairs = cu_pairs_for(items);
         if constexpr (kSplitDkDv<D>) {
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, LENS, 1>), dim3((unsigned)p.num_units), dim3(256), 0,
                                stream, p);

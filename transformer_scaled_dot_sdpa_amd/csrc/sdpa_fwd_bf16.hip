@@ -175,19 +175,26 @@ fwd_bf16_kernel(KParams p) {
     // workgroup_units and item_block for the schedule and the order)
     int unit_first, unit_step, unit_last;
     workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
+    if (p.cu_pairs > 0) unit_first = cu_pair_unit(p.num_units, p.cu_pairs, unit_first);
     for (int unit = unit_first; unit < unit_last; unit += unit_step)
     for (int k_item = 0; k_item < p.upi; ++k_item) {
     int item;
-    if (LENS && p.lens_pairs) {
+    if (LENS && p.lens_pairs == 1) {
         // items u and num_items - 1 - u: a long one and a short one
         item = k_item == 0 ? unit : p.num_items - 1 - unit;
         if (k_item == 1 && item <= unit) break;   // the middle item of an odd count runs once
+    } else if (LENS && p.lens_pairs == 2) {
+        // one item per unit, in length-rank order interleaved from both
+        // ends: units 2k and 2k + 1 (one compute unit, see cu_pair_unit)
+        // take the k-th longest and the k-th shortest item
+        item = (unit & 1) ? p.num_items - 1 - (unit >> 1) : (unit >> 1);
     } else {
         item = unit * p.upi + k_item;
         if (item >= p.num_items) break;
     }
     int bh, qb;
     if (LENS && p.lens_pairs) {
+        // item = position in the length ranking: batch s_order[r]
         const int per_b = p.H * p.num_qb;
         const int r = item / per_b, rem = item - r * per_b;
         const int hq = rem / p.num_qb;
@@ -261,6 +268,46 @@ fwd_bf16_kernel(KParams p) {
     const __amdgpu_buffer_rsrc_t mrsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(mg), (short)0, (int)m_bytes, 0x00020000);
     const uint32_t m_row_off = MASK ? (uint32_t)(qrow < p.Lq ? qrow : p.Lq - 1) * p.m_sl * 4 : 0u;
+    // this lane's mask values for one tile: 16 keys per 32-key sub-tile
+    // (two runs of 8 consecutive keys).  The first sub-tile's values are
+    // loaded one tile ahead, between the softmax and the P.V products, so
+    // that they arrive under those products and the tile barrier; the
+    // others at the start of their tile, under the first sub-tile's S
+    // products.  (All of them one tile ahead needs 32 more registers than
+    // two wavefronts per SIMD leave, and the spills cost more than the
+    // latency saved: measured on MI355X.)  The mask kernels also read V
+    // operands one key step ahead instead of two, for the same registers.
+    constexpr int MPF = 1;   // sub-tiles whose mask values are loaded a tile ahead
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 mb[MASK ? NKT : 1][4];
+    auto load_mask = [&](int t, int kt) __attribute__((always_inline)) {
+        if constexpr (MASK) {
+            const int ts = t * BC;
+            if (p.mask_vec) {   // 16-byte aligned rows: one 16-byte load per 4 keys
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int key = ts + kt * 32 + 16 * (j >> 1) + 8 * h + 4 * (j & 1);
+                    mb[kt][j] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(mrsrc, m_row_off + key * 4, 0, 0));
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = ts + kt * 32 + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + e;
+                        mb[kt][j][e] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(mrsrc, m_row_off + key * 4, 0, 0));
+                    }
+            }
+        }
+    };
+    // the next tile's K/V loads and mask loads, for a tile this wavefront skips
+    auto skip_tile = [&](int lt, int lb) __attribute__((always_inline)) {
+        issue_loads(lt, lb);
+#pragma unroll
+        for (int kt = 0; kt < (MPF < NKT ? MPF : NKT); ++kt) load_mask(lt, kt);
+    };
 
     f32x16 o[NDT];
 #pragma unroll
@@ -283,33 +330,9 @@ fwd_bf16_kernel(KParams p) {
     auto tile_math = [&](auto FAST, int t, const uint16_t* Ks, const uint16_t* Vs, int lt,
                          int lb) __attribute__((always_inline)) {
         const int ts = t * BC;
-        // mask values of this lane's 16 keys per sub-tile (two runs of 8
-        // consecutive keys), fetched before the products so they arrive
-        // under them
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        f32x4 mb[MASK ? NKT : 1][4];
         if constexpr (MASK) {
-            if (p.mask_vec) {   // 16-byte aligned rows: one 16-byte load per 4 keys
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int key = ts + kt * 32 + 16 * (j >> 1) + 8 * h + 4 * (j & 1);
-                        mb[kt][j] = __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(mrsrc, m_row_off + key * 4, 0, 0));
-                    }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int key = ts + kt * 32 + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + e;
-                            mb[kt][j][e] = __builtin_bit_cast(
-                                float, __builtin_amdgcn_raw_buffer_load_b32(mrsrc, m_row_off + key * 4, 0, 0));
-                        }
-            }
+            for (int kt = (MPF < NKT ? MPF : NKT); kt < NKT; ++kt) load_mask(t, kt);
         }
         // S^T = K Q^T, one 32-key sub-tile after the other so the softmax of
         // the first can start under the MFMAs of the second; operand reads
@@ -343,14 +366,17 @@ fwd_bf16_kernel(KParams p) {
         // masks: padding / ragged tail and the causal diagonal
         const bool need_mask = (ts + BC > kv_len) || (CAUSAL && ts + BC - 1 > q0w);
         if (need_mask) {
+            // key ts + 8h + off is valid when off < lim: below kv_len and, with
+            // the causal mask, at most qrow.  One bound per tile against
+            // constant offsets (per-element key indices would otherwise be
+            // kept in registers across the loop).
+            const int lim = (CAUSAL ? min(kv_len, qrow + 1) : kv_len) - ts - 8 * h;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = ts + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-                    bool ok = key < kv_len;
-                    if (CAUSAL) ok = ok && key <= qrow;
-                    s[kt][r] = ok ? s[kt][r] : -INFINITY;
+                    const int off = kt * 32 + 16 * (r >> 3) + (r & 7);
+                    s[kt][r] = off < lim ? s[kt][r] : -INFINITY;
                 }
         }
 
@@ -358,7 +384,7 @@ fwd_bf16_kernel(KParams p) {
         // softmax, whose vector work covers their latency
         constexpr int NSTEP = 2 * NKT;
         // V operand reads run RA key steps ahead
-        constexpr int RA = 2;
+        constexpr int RA = MASK ? 1 : 2;
         constexpr int VA = RA + 1;
         i16x8 va[VA][NDT];
         auto read_v = [&](int step, i16x8* dst) __attribute__((always_inline)) {
@@ -434,6 +460,12 @@ fwd_bf16_kernel(KParams p) {
                 }
         }
 
+        // the next tile's mask values, now that the scores' registers are free
+        if (MASK && lt >= 0) {
+#pragma unroll
+            for (int kt = 0; kt < (MPF < NKT ? MPF : NKT); ++kt) load_mask(lt, kt);
+        }
+
         // O^T += V^T P^T over 2*NKT key steps of 16; the NDT output chains
         // interleave, the transposed V reads run two key steps ahead and the
         // V loads of the next tile are spread over the steps.
@@ -463,27 +495,27 @@ fwd_bf16_kernel(KParams p) {
         return t < ntiles ? t : -1;
     };
     auto run_pass = [&](auto TAIL) __attribute__((always_inline)) {
-        issue_loads(tile_of(0), 0);
+        if (tile_of(0) >= 0) skip_tile(tile_of(0), 0);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         {
             const int t0 = tile_of(0);
             if (t0 >= 0 && t0 * BC < wave_kv_end)
                 tile_math(std::false_type(), t0, kb0, vb0, tile_of(1), 1);
-            else if (tile_of(1) >= 0) issue_loads(tile_of(1), 1);
+            else if (tile_of(1) >= 0) skip_tile(tile_of(1), 1);
         }
         for (int r = 1; r < nsteps; r += 2) {
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
             const int c0 = tile_of(r), l0 = r + 1 < nsteps ? tile_of(r + 1) : -1;
             if (c0 >= 0 && c0 * BC < wave_kv_end) tile_math(TAIL, c0, kb1, vb1, l0, 0);
-            else if (l0 >= 0) issue_loads(l0, 0);
+            else if (l0 >= 0) skip_tile(l0, 0);
             if (r + 1 >= nsteps) break;
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
             const int c1 = tile_of(r + 1), l1 = r + 2 < nsteps ? tile_of(r + 2) : -1;
             if (c1 >= 0 && c1 * BC < wave_kv_end) tile_math(TAIL, c1, kb0, vb0, l1, 1);
-            else if (l1 >= 0) issue_loads(l1, 1);
+            else if (l1 >= 0) skip_tile(l1, 1);
         }
         // zero-length loads of the last tile may still be in flight
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -581,7 +613,8 @@ fwd_bf16_kernel(KParams p) {
 }
 
 template <int D, int DV, int BC, int NW, int KS, bool CAUSAL, bool LENS, bool MASK>
-hipError_t launch_one(const FwdArgs& a, bool pairs, hipStream_t stream) {
+hipError_t launch_one(const FwdArgs& a, int sched, hipStream_t stream) {
+    const bool pairs = sched == 1;
     constexpr int BR = NW * 32;
     auto kern = fwd_bf16_kernel<D, DV, BC, NW, KS, CAUSAL, LENS, MASK>;
     KParams p;
@@ -617,10 +650,26 @@ hipError_t launch_one(const FwdArgs& a, bool pairs, hipStream_t stream) {
     const long long slots = (long long)(a.num_cus > 0 ? a.num_cus : 256) * fwd_blocks_per_cu<NW, KS>();
     p.upi = (CAUSAL && items > slots) ? 2 : 1;
     p.B = a.B;
+    // Compute-unit pairs (default schedule): when every workgroup is
+    // resident at once and some compute units hold two, renumber the units
+    // so that each such compute unit runs a long item and a short one
+    // (cu_pair_unit).  Causal query blocks already alternate long and short
+    // (an even count per slice keeps the alternation aligned); with key
+    // lengths the items are taken in length-rank order interleaved from both
+    // ends (from 5 key tiles up: shorter key ranges measured no gain).
     p.lens_pairs = 0;
+    p.cu_pairs = 0;
+    const int cus = a.num_cus > 0 ? a.num_cus : 256;
+    const bool cu_pairing = sched == 0 && items <= slots && items > cus && fwd_blocks_per_cu<NW, KS>() == 2 &&
+                            cus % 8 == 0;
     if (LENS && !CAUSAL && pairs && a.B > 1 && a.B <= kMaxPairBatches) {
         p.lens_pairs = 1;
         p.upi = 2;
+    } else if (LENS && !CAUSAL && cu_pairing && (a.Lk + 63) / 64 >= 5 && a.B > 1 && a.B <= kMaxPairBatches) {
+        p.lens_pairs = 2;
+        p.cu_pairs = cus / 8;
+    } else if (CAUSAL && cu_pairing && p.upi == 1 && p.num_qb % 2 == 0) {
+        p.cu_pairs = cus / 8;
     }
     p.num_units = (int)((items + p.upi - 1) / p.upi);
     const long long nwg = p.num_units;
@@ -629,7 +678,7 @@ hipError_t launch_one(const FwdArgs& a, bool pairs, hipStream_t stream) {
 }
 
 template <int D, int DV, int BC, int NW, int KS, bool MASK>
-hipError_t launch_d(const FwdArgs& a, bool pairs, hipStream_t s) {
+hipError_t launch_d(const FwdArgs& a, int pairs, hipStream_t s) {
     const bool lens = a.key_lens != nullptr;
     if (a.causal)
         return lens ? launch_one<D, DV, BC, NW, KS, true, true, MASK>(a, pairs, s)
@@ -641,7 +690,7 @@ hipError_t launch_d(const FwdArgs& a, bool pairs, hipStream_t s) {
 // default tiles (64 keys, 4 wavefronts, no key split) for every (d_k, d_v)
 // pair, with and without the additive mask
 template <int D, int DV>
-hipError_t launch_default(const FwdArgs& a, bool pairs, hipStream_t s) {
+hipError_t launch_default(const FwdArgs& a, int pairs, hipStream_t s) {
     return a.mask != nullptr ? launch_d<D, DV, 64, 4, 1, true>(a, pairs, s)
                              : launch_d<D, DV, 64, 4, 1, false>(a, pairs, s);
 }
@@ -650,7 +699,7 @@ hipError_t launch_default(const FwdArgs& a, bool pairs, hipStream_t s) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s) {
     if (t.d != a.d) return hipErrorInvalidValue;
-    const bool pairs = t.pairs != 0;
+    const int pairs = t.pairs;   // 0 (default, with compute-unit pairs) or 1 (key-length pairs)
     if (t.bc == 64 && t.waves == 4 && t.ks == 1) {
         if (a.d == 128 && a.dv == 128) return launch_default<128, 128>(a, pairs, s);
         if (a.d == 128 && a.dv == 64) return launch_default<128, 64>(a, pairs, s);

@@ -11,30 +11,31 @@
 //            min(Lq, Lk))
 //
 //   bf16_d*_bc64_w4       default: 4 wavefronts (128 rows) per workgroup,
-//                         2 per CU; the only tile with d_v != d_k and masks
+//                         2 per CU; the only tile with d_v != d_k and masks.
+//                         Between one and two rounds of slots it runs one
+//                         item per workgroup, renumbered so that the two
+//                         workgroups of a CU take a long and a short item
+//                         (cu_pair_unit), which balances causal blocks and
+//                         ranked key lengths alike.
 //   bf16_d128_bc64_w4_ks2 two groups of 4 wavefronts take alternate key
 //                         tiles of the same 128 rows (1 workgroup per CU):
-//                         half the tile steps per item.  Wins when the
-//                         items are too few to keep the slots busy and
-//                         their key ranges are long: causal problems of at
-//                         most 2 items per CU with >= 32 steps (the longest
-//                         items set the time), non-causal ones of at most 1
-//                         item per CU with >= 16 steps.
+//                         half the tile steps per item.  Wins when there is
+//                         at most one item per CU and the key ranges are
+//                         long: >= 32 steps causal, >= 16 otherwise.
 //   bf16_d*_bc64_w8       8 wavefronts (256 rows) share each K/V tile, 1
 //                         workgroup per CU: half the L2->LDS bytes per flop.
-//                         Wins for 2..4 items per CU with >= 16 steps and no
-//                         key lengths (d64: at most 64 steps, and >= 32 above
-//                         2 items per CU).
+//                         Wins for 2..4 items per CU (causal: above 2) with
+//                         >= 16 steps and no key lengths (d64: at most 64
+//                         steps, and >= 32 above 2 items per CU).
 //   bf16_d*_bc64_w4_pairs per-batch key lengths, no causal mask: batches
 //                         ranked by length, each workgroup runs the i-th
 //                         longest and the i-th shortest item.  Wins when the
-//                         items need between one and two rounds of slots
-//                         (balanced pairs fill one round); loses when they
-//                         fit in one round (every item starts at once).
+//                         items need between two and four rounds of slots.
 //
-// The thresholds come from timing every tile on 34 shapes on MI355X
+// The thresholds come from timing every tile on 39 shapes on MI355X
 // (interleaved batches, median of 3); the design notes list the table.  On
-// 33 of them the choice is within 2% of the fastest tile, on one 4% off.
+// 37 of them the choice is within 2% of the fastest tile; the two others
+// changed places between sweeps.
 #include <string.h>
 
 #include "sdpa_internal.h"
@@ -78,11 +79,10 @@ bool select_bf16_tile(int d, int causal, int has_key_lens, long long bh, int Lq,
     const char* name = d == 128 ? "bf16_d128_bc64_w4" : "bf16_d64_bc64_w4";
     if (has_key_lens && !causal && items > 2 * cus && items <= 4 * cus) {
         name = d == 128 ? "bf16_d128_bc64_w4_pairs" : "bf16_d64_bc64_w4_pairs";
-    } else if (!general && d == 128 && ((causal && items <= 2 * cus && steps >= 32) ||
-                                        (!causal && items <= cus && steps >= 16))) {
+    } else if (!general && d == 128 && items <= cus && steps >= (causal ? 32 : 16)) {
         name = "bf16_d128_bc64_w4_ks2";
-    } else if (!general && !has_key_lens && items >= 2 * cus && items <= 4 * cus && steps >= 16 &&
-               (d == 128 || (steps <= 64 && (items <= 2 * cus || steps >= 32)))) {
+    } else if (!general && !has_key_lens && (causal ? items > 2 * cus : items >= 2 * cus) && items <= 4 * cus &&
+               steps >= 16 && (d == 128 || (steps <= 64 && (items <= 2 * cus || steps >= 32)))) {
         name = d == 128 ? "bf16_d128_bc64_w8" : "bf16_d64_bc64_w8";
     }
     *out = *tile_named(d, name);

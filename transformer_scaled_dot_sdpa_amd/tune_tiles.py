@@ -36,6 +36,8 @@ SHAPES = [
     (128, 4, 32, 1024, 1024, False, (256, 1024)), (128, 4, 16, 512, 512, True, None),
     (128, 2, 32, 1024, 1024, True, None), (128, 1, 16, 2048, 2048, True, None), (128, 1, 64, 2048, 2048, True, None),
     (128, 1, 16, 4096, 4096, False, None), (128, 2, 8, 8192, 8192, True, None), (128, 16, 16, 512, 512, True, None),
+    (128, 32, 8, 256, 256, True, None), (64, 2, 80, 256, 256, True, None), (64, 8, 40, 128, 300, False, (64, 300)),
+    (128, 8, 40, 128, 512, False, (64, 512)), (128, 1, 32, 2048, 2048, True, None), (128, 4, 16, 2048, 2048, True, None),
 ]
 QUICK = [SHAPES[i] for i in (0, 1, 2, 18, 19, 22, 28)]
 
@@ -95,7 +97,7 @@ def main():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     print("| d_k | B·H | Lq × Lk | causal | key lengths | items per CU | steps | "
           + " | ".join(t.split("_", 2)[2] for t in TILES[128]) + " | chosen, µs |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    print("|---|---|---|---|---|---|---|" + "---|" * len(TILES[128]) + "---|")
     off = []
     for (d, B, H, Lq, Lk, causal, kl) in (QUICK if args.quick else SHAPES):
         res, chosen = time_shape(torch, sdpa, d, B, H, Lq, Lk, causal, kl)
