@@ -33,6 +33,17 @@ def test_library_exports_every_declared_symbol():
         assert re.search(rf"\bT {name}$", out, flags=re.M), name
 
 
+def test_binding_sizes_match_header_defines():
+    text = open(HEADER, encoding="utf-8").read()
+
+    def define(name):
+        m = re.search(rf"#define {name} \(\(size_t\)(\d+)(?: << (\d+))?\)", text)
+        assert m, name
+        return int(m.group(1)) << int(m.group(2) or 0)
+
+    assert define("SDPA_DECODE_NOALLOC_SCRATCH_BYTES") == b.DECODE_NOALLOC_SCRATCH_BYTES
+
+
 def test_status_strings():
     for code, name in [(0, "SUCCESS"), (1, "INVALID_VALUE"), (2, "NOT_SUPPORTED"),
                        (3, "HIP_ERROR"), (4, "ALLOC_FAILED")]:

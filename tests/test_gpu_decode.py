@@ -125,6 +125,33 @@ def test_decode_workload_full(name):
     assert_close(o, l, ro, rl, "bf16", name)
 
 
+def test_decode_workspace_reused_across_calls():
+    """One workspace serves calls of different sizes in a row on one stream,
+    each call's partial results overwriting the last call's."""
+    import torch
+    import transformer_scaled_dot_sdpa_amd as sdpa
+    shapes = [(1, 2, 1, 4096, 64, None), (2, 3, 4, 2000, 128, [2000, 7]), (1, 8, 1, 4096, 64, None),
+              (3, 1, 8, 999, 128, [0, 999, 500]), (1, 2, 1, 4096, 64, None)]
+    cases = []
+    for i, (B, H, Lq, Lk, d, kl) in enumerate(shapes):
+        q, k, v, _ = inputs.generate(B, H, Lq, Lk, d, "bf16", 1500 + i)
+        cases.append((q, k, v, kl, d))
+    need = 0
+    dev = []
+    for q, k, v, kl, d in cases:
+        qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+        need = max(need, sdpa.decode_workspace_size(qd, kd))
+        dev.append((qd, kd, vd, torch.from_numpy(np.asarray(kl, np.int32)).cuda() if kl else None))
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    announce(f"decode: {len(cases)} calls sharing one {need}-byte workspace")
+    outs = [sdpa.decode(qd, kd, vd, key_lens=klt, workspace=ws) for qd, kd, vd, klt in dev]
+    torch.cuda.synchronize()
+    for (q, k, v, kl, d), (o, l) in zip(cases, outs):
+        ro, rl = oracle_ref(q, k, v, "bf16", False, kl)
+        assert_close(o.float().cpu().numpy(), l.cpu().numpy(), ro, rl, "bf16", f"reused workspace {q.shape}")
+
+
 def test_decode_agrees_with_forward():
     """Both entry points compute the same function; on the same inputs they
     differ only by rounding."""

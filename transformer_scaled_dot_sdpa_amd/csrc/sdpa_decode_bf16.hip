@@ -22,7 +22,12 @@
 //   result is written as out/lse directly; otherwise the chunk's normalised
 //   o and natural-log lse go to the workspace and decode_combine merges the
 //   chunks: lse = ln sum_c e^{lse_c}, o = sum_c e^{lse_c - lse} o_c, the
-//   same identity with the log-sum-exp of section 広がる学問.
+//   same identity with the log-sum-exp of section 広がる学問.  (Merging in
+//   the workgroup that finishes a slice's last chunk, found with a counter,
+//   saves the second launch but needs a device-scope release and acquire per
+//   workgroup, i.e. L2 write-back and invalidation across the XCDs: on
+//   MI355X that made a call of 8 slices x 32 chunks 17.9 us against 9.7 us
+//   for the two launches.)
 #include "sdpa_internal.h"
 
 #include <math.h>
@@ -96,6 +101,41 @@ __device__ __forceinline__ float across_groups_sum(float x) {
     return x;
 }
 
+// Feature f of output row `row` from the per-chunk results: lse = ln sum_c
+// e^{lse_c}, o = sum_c e^{lse_c - lse} o_c, accumulated with a running
+// maximum over batches of 32 chunks whose loads are all issued before any of
+// them is used (one memory latency per batch).  A row with no valid key in
+// any chunk gets o = 0, lse = -inf.
+template <int D>
+__device__ __forceinline__ void merge_chunks(const DParams& p, size_t rows, size_t row, int f) {
+    constexpr int NB = 32;
+    float M = -INFINITY, Z = 0.f, O = 0.f;
+    for (int c0 = 0; c0 < p.splits; c0 += NB) {
+        float xs[NB], ys[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            // chunks past the last reload the last one (in bounds) and are
+            // dropped below
+            const int c = c0 + j < p.splits ? c0 + j : p.splits - 1;
+            xs[j] = p.part_lse[(size_t)c * rows + row];
+            ys[j] = p.part_o[((size_t)c * rows + row) * D + f];
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const float x = c0 + j < p.splits ? xs[j] : -INFINITY;
+            const float mn = fmaxf(M, x);
+            const float mref = mn == -INFINITY ? 0.f : mn;
+            const float a = __expf(M - mref);                        // 0 while M = -inf
+            const float w = x == -INFINITY ? 0.f : __expf(x - mref);  // 0 for an empty chunk
+            Z = fmaf(Z, a, w);
+            O = fmaf(O, a, w * ys[j]);
+            M = mn;
+        }
+    }
+    p.out[row * D + f] = to_bf16(Z > 0.f ? O / Z : 0.f);
+    if (p.lse != nullptr && f == 0) p.lse[row] = Z > 0.f ? M + logf(Z) : -INFINITY;
+}
+
 template <int D, int NQ>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DParams p) {
     constexpr int CPR = D / 8;          // lanes per key row (16 bytes each)
@@ -122,6 +162,28 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DParams p) {
     }
     const int k_lo = split * p.chunk;
     const int k_hi = min(k_lo + p.chunk, kv_len);
+
+    const uint16_t* kb = p.k + (size_t)bh * p.Lk * D;
+    const uint16_t* vb = p.v + (size_t)bh * p.Lk * D;
+    // this lane's row in step s: k_lo + s * STEP + wave * G + grp.  A lane
+    // whose row is at or past k_hi loads row k_lo instead (in bounds: every
+    // chunk starts below Lk) and masks it, so every batch of UNROLL steps
+    // is loaded whole, without branches.
+    const int row0 = k_lo + wave * G + grp;
+    const int nsteps = (k_hi - k_lo + STEP - 1) / STEP;
+    uint4 kw[UNROLL], vw[UNROLL];
+    auto load_batch = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int row = row0 + (s0 + u) * STEP;
+            const int rr = row < k_hi ? row : k_lo;
+            kw[u] = *reinterpret_cast<const uint4*>(kb + (size_t)rr * D + 8 * c);
+            vw[u] = *reinterpret_cast<const uint4*>(vb + (size_t)rr * D + 8 * c);
+        }
+    };
+    // the first batch goes out before the query rows are read, so that the
+    // two memory latencies overlap
+    if (nsteps > 0) load_batch(0);
 
     // query rows (pre-scaled into exp2 units) and their valid key bounds
     float qv[NQ][8];
@@ -151,14 +213,13 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DParams p) {
         for (int e = 0; e < 8; ++e) o[i][e] = 0.f;
     }
 
-    const uint16_t* kb = p.k + (size_t)bh * p.Lk * D;
-    const uint16_t* vb = p.v + (size_t)bh * p.Lk * D;
-    // this lane's row in step s: k_lo + s * STEP + wave * G + grp
-    const int row0 = k_lo + wave * G + grp;
-
-    auto consume = [&](int row, uint4 kw, uint4 vw) __attribute__((always_inline)) {
-        const uint32_t ka[4] = {kw.x, kw.y, kw.z, kw.w};
-        const uint32_t va[4] = {vw.x, vw.y, vw.z, vw.w};
+    // One key row per lane group: running maximum m (wave-uniform), sum l
+    // and output slice o, rescaled when m grows.  While every row so far
+    // was masked (m = -inf) the reference is 0, so the rescale factor and
+    // the masked weights are exact zeros and nothing branches.
+    auto consume = [&](int row, uint4 kv4, uint4 vv4) __attribute__((always_inline)) {
+        const uint32_t ka[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+        const uint32_t va[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
         float kf[8], vf[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -174,11 +235,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DParams p) {
             for (int e = 0; e < 8; ++e) z = fmaf(qv[i][e], kf[e], z);
             z = group_sum<CPR>(z);
             const bool ok = row < n_valid[i];
-            const float s = ok ? z : -INFINITY;
-            const float mn = fmaxf(m[i], across_groups_max<CPR>(s));
-            if (mn == -INFINITY) continue;   // wave-uniform: nothing valid yet
-            const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);   // 0 when m was -inf
-            const float pj = ok ? __builtin_amdgcn_exp2f(z - mn) : 0.f;
+            const float mn = fmaxf(m[i], across_groups_max<CPR>(ok ? z : -INFINITY));
+            const float mref = mn == -INFINITY ? 0.f : mn;
+            const float alpha = __builtin_amdgcn_exp2f(m[i] - mref);   // 0 when m was -inf
+            const float pj = ok ? __builtin_amdgcn_exp2f(z - mref) : 0.f;
             l[i] = fmaf(l[i], alpha, pj);
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[i][e] = fmaf(o[i][e], alpha, pj * vf[e]);
@@ -186,28 +246,18 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DParams p) {
         }
     };
 
-    // a lane whose row is at or past k_hi loads row k_lo instead (in
-    // bounds, and a row of this chunk) and masks it
-    const int nsteps = (k_hi - k_lo + STEP - 1) / STEP;
-    int s = 0;
-    for (; s + UNROLL <= nsteps; s += UNROLL) {
-        uint4 kw[UNROLL], vw[UNROLL];
+    // batches of UNROLL steps; the next batch's loads go out before the
+    // current one is consumed
+    for (int s = 0; s < nsteps; s += UNROLL) {
+        uint4 kc[UNROLL], vc[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int row = row0 + (s + u) * STEP;
-            const int rr = row < k_hi ? row : k_lo;
-            kw[u] = *reinterpret_cast<const uint4*>(kb + (size_t)rr * D + 8 * c);
-            vw[u] = *reinterpret_cast<const uint4*>(vb + (size_t)rr * D + 8 * c);
+            kc[u] = kw[u];
+            vc[u] = vw[u];
         }
+        if (s + UNROLL < nsteps) load_batch(s + UNROLL);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) consume(row0 + (s + u) * STEP, kw[u], vw[u]);
-    }
-    for (; s < nsteps; ++s) {
-        const int row = row0 + s * STEP;
-        const int rr = row < k_hi ? row : k_lo;
-        const uint4 kw = *reinterpret_cast<const uint4*>(kb + (size_t)rr * D + 8 * c);
-        const uint4 vw = *reinterpret_cast<const uint4*>(vb + (size_t)rr * D + 8 * c);
-        consume(row, kw, vw);
+        for (int u = 0; u < UNROLL; ++u) consume(row0 + (s + u) * STEP, kc[u], vc[u]);
     }
 
     // merge the row groups of the wavefront (same m), then the wavefronts
@@ -257,54 +307,12 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DParams p) {
     }
 }
 
-// One wavefront per output row: lse = ln sum_c e^{lse_c}, o = sum_c
-// e^{lse_c - lse} o_c over the chunks; a row with no valid key in any chunk
-// gets o = 0, lse = -inf.  Lane c handles chunk c (64 at a time) for the
-// weights, which then go through LDS to the feature loop, whose loads are
-// independent of each other.
+// Thread t merges feature t % D of output row t / D (merge_chunks).
 template <int D>
 __global__ void __launch_bounds__(256) decode_combine(DParams p, long long rows) {
-    __shared__ float wsh[4][64];
-    const int wave = threadIdx.x >> 6;
-    const long long row = (long long)blockIdx.x * 4 + wave;
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;   // wave-uniform; no block-wide barrier below
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < p.splits; c0 += 64) {
-        const int c = c0 + lane;
-        const float x = c < p.splits ? p.part_lse[(size_t)c * rows + row] : -INFINITY;
-        M = fmaxf(M, x);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float acc[D / 64];
-#pragma unroll
-    for (int r = 0; r < D / 64; ++r) acc[r] = 0.f;
-    float Z = 0.f;
-    if (M != -INFINITY) {
-        for (int c0 = 0; c0 < p.splits; c0 += 64) {
-            const int c = c0 + lane;
-            const float wc = c < p.splits ? __expf(p.part_lse[(size_t)c * rows + row] - M) : 0.f;   // 0 for an empty chunk
-            float zs = wc;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) zs += __shfl_xor(zs, off);
-            Z += zs;
-            wsh[wave][lane] = wc;
-            __builtin_amdgcn_wave_barrier();
-            const int n = min(64, p.splits - c0);
-#pragma unroll 8
-            for (int j = 0; j < n; ++j) {
-                const float w = wsh[wave][j];
-                const float* src = p.part_o + ((size_t)(c0 + j) * rows + row) * D;
-#pragma unroll
-                for (int r = 0; r < D / 64; ++r) acc[r] = fmaf(w, src[lane + 64 * r], acc[r]);
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < D / 64; ++r) p.out[row * D + lane + 64 * r] = to_bf16(Z > 0.f ? acc[r] / Z : 0.f);
-    if (p.lse != nullptr && lane == 0) p.lse[row] = Z > 0.f ? M + logf(Z) : -INFINITY;
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= rows * D) return;
+    merge_chunks<D>(p, (size_t)rows, (size_t)(t / D), (int)(t % D));
 }
 
 template <int D, int NQ>
@@ -331,7 +339,8 @@ hipError_t launch_nq(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s)
     hipLaunchKernelGGL((decode_kernel<D, NQ>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
-    hipLaunchKernelGGL((decode_combine<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, rows);
+    const long long threads = rows * D;
+    hipLaunchKernelGGL((decode_combine<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p, rows);
     return hipGetLastError();
 }
 
