@@ -131,6 +131,7 @@ CASES = [
     # causal, an even number of blocks per slice, between one and two blocks
     # per compute unit: the kernels renumber their units in compute-unit pairs
     (2, 80, 256, 256, True, None),
+    (1, 135, 256, 256, True, None),
 ]
 
 

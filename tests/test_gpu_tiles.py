@@ -47,6 +47,11 @@ CASES = [
     # unit, 5 key tiles: the default tile orders items by length rank
     # interleaved from both ends and pairs them per compute unit
     (8, 40, 100, 300, False, [300, 5, 0, 150, 299, 64, 1, 200]),
+    # the same two schedules with an odd number of items (the middle item of
+    # the length order, and XCD ranges that start at an odd unit and keep
+    # the plain order)
+    (3, 91, 100, 320, False, [320, 7, 200]),
+    (1, 135, 256, 256, True, None),
 ]
 
 
