@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 TILES = {
     128: ["bf16_d128_bc64_w4", "bf16_d128_bc64_w4_pairs", "bf16_d128_bc64_w4_ks2", "bf16_d128_bc64_w8"],
-    64: ["bf16_d64_bc64_w4", "bf16_d64_bc64_w4_pairs", "bf16_d64_bc64_w8"],
+    64: ["bf16_d64_bc64_w4", "bf16_d64_bc64_w4_pairs", "bf16_d64_bc64_w4_ks2", "bf16_d64_bc64_w8"],
 }
 TILE_PARAMS = [(d, t) for d, ts in TILES.items() for t in ts]
 

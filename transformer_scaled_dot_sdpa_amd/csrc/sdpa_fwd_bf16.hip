@@ -61,16 +61,22 @@ using namespace bf16k;
 // D: width of queries and keys; DV: width of values and outputs.  MASK adds
 // an fp32 bias to the scaled scores.  Tensor rows are addressed through the
 // strides in KParams (contiguous or head-interleaved layouts alike).
-// Every tile configuration runs two wavefronts per SIMD (the second
-// __launch_bounds__ argument, which caps a wavefront at 256 registers):
-// 8 / (NW * KS) workgroups per compute unit, at least one.
-template <int NW, int KS>
+// Tile configurations run two wavefronts per SIMD (the second
+// __launch_bounds__ argument, which caps a wavefront at 256 registers),
+// except the d64 key split, which fits four (128 registers, V operands read
+// one key step ahead): 4 * waves-per-SIMD / (NW * KS) workgroups per
+// compute unit, at least one.
+template <int D, int KS>
+constexpr int fwd_waves_per_simd() {
+    return (D == 64 && KS == 2) ? 4 : 2;
+}
+template <int D, int NW, int KS>
 constexpr int fwd_blocks_per_cu() {
-    return 8 / (NW * KS) > 0 ? 8 / (NW * KS) : 1;
+    return 4 * fwd_waves_per_simd<D, KS>() / (NW * KS) > 0 ? 4 * fwd_waves_per_simd<D, KS>() / (NW * KS) : 1;
 }
 
 template <int D, int DV, int BC, int NW, int KS, bool CAUSAL, bool LENS, bool MASK>
-__global__ void __launch_bounds__(NW * KS * 64, 2)
+__global__ void __launch_bounds__(NW * KS * 64, (fwd_waves_per_simd<D, KS>()))
 fwd_bf16_kernel(KParams p) {
     static_assert(KS == 1 || KS == 2, "key split of 1 or 2 groups");
     constexpr int NT = NW * 64;                // threads of one group
@@ -384,7 +390,7 @@ fwd_bf16_kernel(KParams p) {
         // softmax, whose vector work covers their latency
         constexpr int NSTEP = 2 * NKT;
         // V operand reads run RA key steps ahead
-        constexpr int RA = MASK ? 1 : 2;
+        constexpr int RA = (MASK || fwd_waves_per_simd<D, KS>() > 2) ? 1 : 2;
         constexpr int VA = RA + 1;
         i16x8 va[VA][NDT];
         auto read_v = [&](int step, i16x8* dst) __attribute__((always_inline)) {
@@ -647,7 +653,7 @@ hipError_t launch_one(const FwdArgs& a, int sched, hipStream_t stream) {
     // long/short pairs of equal length once there are more items than
     // resident workgroups; a smaller problem takes one item per workgroup so
     // that every item starts at once.
-    const long long slots = (long long)(a.num_cus > 0 ? a.num_cus : 256) * fwd_blocks_per_cu<NW, KS>();
+    const long long slots = (long long)(a.num_cus > 0 ? a.num_cus : 256) * fwd_blocks_per_cu<D, NW, KS>();
     p.upi = (CAUSAL && items > slots) ? 2 : 1;
     p.B = a.B;
     // Compute-unit pairs (default schedule): when every workgroup is
@@ -660,7 +666,7 @@ hipError_t launch_one(const FwdArgs& a, int sched, hipStream_t stream) {
     p.lens_pairs = 0;
     p.cu_pairs = 0;
     const int cus = a.num_cus > 0 ? a.num_cus : 256;
-    const bool cu_pairing = sched == 0 && items <= slots && items > cus && fwd_blocks_per_cu<NW, KS>() == 2 &&
+    const bool cu_pairing = sched == 0 && items <= slots && items > cus && fwd_blocks_per_cu<D, NW, KS>() == 2 &&
                             cus % 8 == 0;
     if (LENS && !CAUSAL && pairs && a.B > 1 && a.B <= kMaxPairBatches) {
         p.lens_pairs = 1;
@@ -668,7 +674,9 @@ hipError_t launch_one(const FwdArgs& a, int sched, hipStream_t stream) {
     } else if (LENS && !CAUSAL && cu_pairing && (a.Lk + 63) / 64 >= 5 && a.B > 1 && a.B <= kMaxPairBatches) {
         p.lens_pairs = 2;
         p.cu_pairs = cus / 8;
-    } else if (CAUSAL && cu_pairing && p.upi == 1 && p.num_qb % 2 == 0) {
+    } else if (CAUSAL && cu_pairing && p.upi == 1 && p.num_qb % 2 == 0 &&
+               (D == 64 || (a.Lq < a.Lk ? a.Lq : a.Lk) > 4 * 64)) {
+        // (d128 with at most 4 key tiles per row measured 8% slower paired)
         p.cu_pairs = cus / 8;
     }
     p.num_units = (int)((items + p.upi - 1) / p.upi);
@@ -712,6 +720,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, const Bf16Tile& t, hipStream_t s) {
     if (t.d == 128 && t.bc == 64 && t.waves == 4 && t.ks == 2) return launch_d<128, 128, 64, 4, 2, false>(a, pairs, s);
     if (t.d == 128 && t.bc == 64 && t.waves == 8 && t.ks == 1) return launch_d<128, 128, 64, 8, 1, false>(a, pairs, s);
     if (t.d == 64 && t.bc == 64 && t.waves == 8 && t.ks == 1) return launch_d<64, 64, 64, 8, 1, false>(a, pairs, s);
+    if (t.d == 64 && t.bc == 64 && t.waves == 4 && t.ks == 2) return launch_d<64, 64, 64, 4, 2, false>(a, pairs, s);
     return hipErrorInvalidValue;
 }
 

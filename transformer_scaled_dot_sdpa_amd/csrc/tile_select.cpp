@@ -17,11 +17,14 @@
 //                         workgroups of a CU take a long and a short item
 //                         (cu_pair_unit), which balances causal blocks and
 //                         ranked key lengths alike.
-//   bf16_d128_bc64_w4_ks2 two groups of 4 wavefronts take alternate key
-//                         tiles of the same 128 rows (1 workgroup per CU):
-//                         half the tile steps per item.  Wins when there is
-//                         at most one item per CU and the key ranges are
-//                         long: >= 32 steps causal, >= 16 otherwise.
+//   bf16_d*_bc64_w4_ks2   two groups of 4 wavefronts take alternate key
+//                         tiles of the same 128 rows: half the tile steps
+//                         per item.  d128: 1 workgroup per CU; wins with at
+//                         most one item per CU and long key ranges (>= 32
+//                         steps causal, >= 16 otherwise).  d64: 4 wavefronts
+//                         per SIMD (128 registers), 2 workgroups per CU;
+//                         wins with at most one item per CU and >= 16 steps,
+//                         or causal with at most two and >= 32 steps.
 //   bf16_d*_bc64_w8       8 wavefronts (256 rows) share each K/V tile, 1
 //                         workgroup per CU: half the L2->LDS bytes per flop.
 //                         Wins for 2..4 items per CU (causal: above 2) with
@@ -34,8 +37,7 @@
 //
 // The thresholds come from timing every tile on 39 shapes on MI355X
 // (interleaved batches, median of 3); the design notes list the table.  On
-// 37 of them the choice is within 2% of the fastest tile; the two others
-// changed places between sweeps.
+// all of them the choice is within 2% of the fastest tile.
 #include <string.h>
 
 #include "sdpa_internal.h"
@@ -52,6 +54,7 @@ const Bf16Tile kTiles[] = {
     {128, 64, 8, 1, 0, "bf16_d128_bc64_w8"},
     {64, 64, 4, 1, 0, "bf16_d64_bc64_w4"},
     {64, 64, 4, 1, 1, "bf16_d64_bc64_w4_pairs"},
+    {64, 64, 4, 2, 0, "bf16_d64_bc64_w4_ks2"},
     {64, 64, 8, 1, 0, "bf16_d64_bc64_w8"},
 };
 
@@ -81,6 +84,8 @@ bool select_bf16_tile(int d, int causal, int has_key_lens, long long bh, int Lq,
         name = d == 128 ? "bf16_d128_bc64_w4_pairs" : "bf16_d64_bc64_w4_pairs";
     } else if (!general && d == 128 && items <= cus && steps >= (causal ? 32 : 16)) {
         name = "bf16_d128_bc64_w4_ks2";
+    } else if (!general && d == 64 && (causal ? items <= 2 * cus && steps >= 32 : items <= cus && steps >= 16)) {
+        name = "bf16_d64_bc64_w4_ks2";
     } else if (!general && !has_key_lens && (causal ? items > 2 * cus : items >= 2 * cus) && items <= 4 * cus &&
                steps >= 16 && (d == 128 || (steps <= 64 && (items <= 2 * cus || steps >= 32)))) {
         name = d == 128 ? "bf16_d128_bc64_w8" : "bf16_d64_bc64_w8";

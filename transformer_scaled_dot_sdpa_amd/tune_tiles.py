@@ -19,7 +19,7 @@ import sys
 import time
 
 TILES = {128: ["bf16_d128_bc64_w4", "bf16_d128_bc64_w4_pairs", "bf16_d128_bc64_w4_ks2", "bf16_d128_bc64_w8"],
-         64: ["bf16_d64_bc64_w4", "bf16_d64_bc64_w4_pairs", "bf16_d64_bc64_w8"]}
+         64: ["bf16_d64_bc64_w4", "bf16_d64_bc64_w4_pairs", "bf16_d64_bc64_w4_ks2", "bf16_d64_bc64_w8"]}
 
 # (d_k, B, H, Lq, Lk, causal, key-length range or None)
 SHAPES = [
