@@ -63,20 +63,21 @@ using namespace bf16k;
 // strides in KParams (contiguous or head-interleaved layouts alike).
 // Tile configurations run two wavefronts per SIMD (the second
 // __launch_bounds__ argument, which caps a wavefront at 256 registers),
-// except the d64 key split, which fits four (128 registers, V operands read
-// one key step ahead): 4 * waves-per-SIMD / (NW * KS) workgroups per
-// compute unit, at least one.
-template <int D, int KS>
+// except the d64 key split and d64 8-wavefront tiles, which fit four (128
+// registers, V operands read one key step ahead): 4 * waves-per-SIMD /
+// (NW * KS) workgroups per compute unit, at least one.
+template <int D, int NW, int KS>
 constexpr int fwd_waves_per_simd() {
-    return (D == 64 && KS == 2) ? 4 : 2;
+    return (D == 64 && (KS == 2 || NW == 8)) ? 4 : 2;
 }
 template <int D, int NW, int KS>
 constexpr int fwd_blocks_per_cu() {
-    return 4 * fwd_waves_per_simd<D, KS>() / (NW * KS) > 0 ? 4 * fwd_waves_per_simd<D, KS>() / (NW * KS) : 1;
+    return 4 * fwd_waves_per_simd<D, NW, KS>() / (NW * KS) > 0 ? 4 * fwd_waves_per_simd<D, NW, KS>() / (NW * KS)
+                                                                 : 1;
 }
 
 template <int D, int DV, int BC, int NW, int KS, bool CAUSAL, bool LENS, bool MASK>
-__global__ void __launch_bounds__(NW * KS * 64, (fwd_waves_per_simd<D, KS>()))
+__global__ void __launch_bounds__(NW * KS * 64, (fwd_waves_per_simd<D, NW, KS>()))
 fwd_bf16_kernel(KParams p) {
     static_assert(KS == 1 || KS == 2, "key split of 1 or 2 groups");
     constexpr int NT = NW * 64;                // threads of one group
@@ -390,7 +391,7 @@ fwd_bf16_kernel(KParams p) {
         // softmax, whose vector work covers their latency
         constexpr int NSTEP = 2 * NKT;
         // V operand reads run RA key steps ahead
-        constexpr int RA = (MASK || fwd_waves_per_simd<D, KS>() > 2) ? 1 : 2;
+        constexpr int RA = (MASK || fwd_waves_per_simd<D, NW, KS>() > 2) ? 1 : 2;
         constexpr int VA = RA + 1;
         i16x8 va[VA][NDT];
         auto read_v = [&](int step, i16x8* dst) __attribute__((always_inline)) {

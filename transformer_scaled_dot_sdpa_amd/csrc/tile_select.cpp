@@ -25,17 +25,19 @@
 //                         per SIMD (128 registers), 2 workgroups per CU;
 //                         wins with at most one item per CU and >= 16 steps,
 //                         or causal with at most two and >= 32 steps.
-//   bf16_d*_bc64_w8       8 wavefronts (256 rows) share each K/V tile, 1
-//                         workgroup per CU: half the L2->LDS bytes per flop.
-//                         Wins for 2..4 items per CU (causal: above 2) with
-//                         >= 16 steps and no key lengths (d64: at most 64
-//                         steps, and >= 32 above 2 items per CU).
+//   bf16_d*_bc64_w8       8 wavefronts (256 rows) share each K/V tile:
+//                         half the L2->LDS bytes per flop.  d128: 1
+//                         workgroup per CU; d64: four wavefronts per SIMD,
+//                         2 workgroups per CU.  Wins with no key lengths for
+//                         2..4 items per CU (causal: above 2) with >= 16
+//                         steps (d64: at most 64 steps, and >= 32 above 2
+//                         items per CU), and at d64 from 4 items per CU on.
 //   bf16_d*_bc64_w4_pairs per-batch key lengths, no causal mask: batches
 //                         ranked by length, each workgroup runs the i-th
 //                         longest and the i-th shortest item.  Wins when the
 //                         items need between two and four rounds of slots.
 //
-// The thresholds come from timing every tile on 39 shapes on MI355X
+// The thresholds come from timing every tile on 42 shapes on MI355X
 // (interleaved batches, median of 3); the design notes list the table.  On
 // all of them the choice is within 2% of the fastest tile.
 #include <string.h>
@@ -86,8 +88,10 @@ bool select_bf16_tile(int d, int causal, int has_key_lens, long long bh, int Lq,
         name = "bf16_d128_bc64_w4_ks2";
     } else if (!general && d == 64 && (causal ? items <= 2 * cus && steps >= 32 : items <= cus && steps >= 16)) {
         name = "bf16_d64_bc64_w4_ks2";
-    } else if (!general && !has_key_lens && (causal ? items > 2 * cus : items >= 2 * cus) && items <= 4 * cus &&
-               steps >= 16 && (d == 128 || (steps <= 64 && (items <= 2 * cus || steps >= 32)))) {
+    } else if (!general && !has_key_lens &&
+               (((causal ? items > 2 * cus : items >= 2 * cus) && items <= 4 * cus && steps >= 16 &&
+                 (d == 128 || (steps <= 64 && (items <= 2 * cus || steps >= 32)))) ||
+                (d == 64 && items >= 4 * cus))) {
         name = d == 128 ? "bf16_d128_bc64_w8" : "bf16_d64_bc64_w8";
     }
     *out = *tile_named(d, name);

@@ -38,6 +38,7 @@ SHAPES = [
     (128, 1, 16, 4096, 4096, False, None), (128, 2, 8, 8192, 8192, True, None), (128, 16, 16, 512, 512, True, None),
     (128, 32, 8, 256, 256, True, None), (64, 2, 80, 256, 256, True, None), (64, 8, 40, 128, 300, False, (64, 300)),
     (128, 8, 40, 128, 512, False, (64, 512)), (128, 1, 32, 2048, 2048, True, None), (128, 4, 16, 2048, 2048, True, None),
+    (64, 32, 16, 1024, 1024, True, None), (64, 64, 16, 512, 512, False, None), (64, 4, 32, 2048, 2048, False, None),
 ]
 QUICK = [SHAPES[i] for i in (0, 1, 2, 18, 19, 22, 28)]
 
