@@ -37,6 +37,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import hashlib
 import json
 import os
 import re
@@ -195,10 +196,30 @@ def cmd_str(argv: list[str]) -> str:
     return " ".join(out)
 
 
-def kernel_source_hash() -> str:
+# Sources behind each leg's kernels.  The forward set is bench.py's own
+# (bench.py trusts a forward traffic summary only while that hash matches);
+# the decode leg may also run the forward kernel.
+LEG_SOURCES = {
+    "backward": ["transformer_scaled_dot_sdpa_amd/csrc/sdpa_bwd_bf16.hip",
+                 "transformer_scaled_dot_sdpa_amd/csrc/sdpa_bwd_f32.hip",
+                 "transformer_scaled_dot_sdpa_amd/csrc/bf16_common.h"],
+    "decode": ["transformer_scaled_dot_sdpa_amd/csrc/sdpa_decode_bf16.hip"],
+}
+
+
+def kernel_source_hash(leg: str = "forward") -> str:
+    """bench.py's hash of the forward kernel sources; for the backward and
+    decode legs the hash of their own kernel sources (decode: followed by
+    the forward sources, whose kernel it runs for many slices)."""
     sys.path.insert(0, ROOT)
     import bench
-    return bench.kernel_source_hash()
+    if leg not in LEG_SOURCES:
+        return bench.kernel_source_hash()
+    h = hashlib.sha256()
+    for rel in LEG_SOURCES[leg] + (bench.KERNEL_SOURCES if leg == "decode" else []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------- summaries
@@ -247,7 +268,7 @@ def write_trace(out_dir, workload, leg, argv, raw, stdout, steps):
     lines += ["", "bench.py's own figure comes from the same profiled run; the kernel trace adds work per "
                   "dispatch, which matters for calls of a few microseconds (there the unprofiled bench.py line is "
                   "the one to quote) and not for kernels of a millisecond.",
-              "", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+              "", f"kernel_source_sha256: {kernel_source_hash(leg)}", ""]
     name = {"forward": "kernel_stats", "backward": "backward_trace", "decode": "decode_trace",
             "forward_ex": "forward_ex"}[leg]
     path = os.path.join(out_dir, f"{workload}_{name}.md")
@@ -332,7 +353,7 @@ def write_traffic(out_dir, workload, leg, cmds, raws, algorithmic_bytes):
     if algorithmic_bytes:
         lines += ["", f"Algorithmic bytes per call (Q, valid K/V rows, O once, lse once): {algorithmic_bytes:.4g}; "
                       f"measured / algorithmic: {total / algorithmic_bytes:.3f} (all kernels of the call)."]
-    lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", f"traffic_bytes_per_launch: {total:.6g}", ""]
+    lines += ["", f"kernel_source_sha256: {kernel_source_hash(leg)}", f"traffic_bytes_per_launch: {total:.6g}", ""]
     path = os.path.join(out_dir, f"{workload}_{'hbm_traffic' if leg == 'forward' else leg + '_hbm_traffic'}.md")
     open(path, "w").write("\n".join(lines))
     print(f"[harness] wrote {path}", flush=True)

@@ -107,3 +107,14 @@ def test_mfma_busy_share_and_clock(tmp_path):
 def test_bench_json_is_found_among_other_output():
     assert rh.bench_json("noise\n{\"metric\": \"m\", \"value\": 1}\n[bench] x\n")["value"] == 1
     assert rh.bench_json("no json here") is None
+
+
+def test_each_leg_hashes_its_own_kernel_sources():
+    # bench.py trusts the forward hash; the backward and decode summaries
+    # carry the hash of the sources their kernels come from
+    fwd = rh.kernel_source_hash("forward")
+    assert fwd == bench.kernel_source_hash() == rh.kernel_source_hash("forward_ex")
+    hashes = {fwd, rh.kernel_source_hash("backward"), rh.kernel_source_hash("decode")}
+    assert len(hashes) == 3
+    for rel in rh.LEG_SOURCES["backward"] + rh.LEG_SOURCES["decode"]:
+        assert os.path.exists(os.path.join(rh.ROOT, rel)), rel
