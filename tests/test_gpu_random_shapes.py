@@ -56,6 +56,29 @@ def test_random_forward_bf16(seed):
     assert_close(o, l, ro, rl, "bf16", what)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_forward_bf16_many_items(seed):
+    """Enough query blocks (about 200 to 1100, i.e. up to four per CU) for the
+    shape-dependent tiles and schedules: compute-unit pairing, key-length
+    ranking, the key split and the 8-wavefront tiles."""
+    rng = np.random.default_rng(5500 + seed)
+    d = int(rng.choice([64, 128]))
+    Lq = int(rng.integers(64, 513))
+    Lk = int(rng.integers(64, 641))
+    causal = bool(rng.random() < 0.5)
+    B = int(rng.integers(1, 9))
+    target = int(rng.integers(200, 1101))
+    H = max(1, round(target / (B * ((Lq + 127) // 128))))
+    kl = _key_lens(rng, B, Lk)
+    what = (f"random fwd bf16 (many items) seed={seed}: B{B} H{H} Lq{Lq} Lk{Lk} d{d} causal={causal} "
+            f"key_lens={kl}")
+    announce(what)
+    q, k, v, _ = inputs.generate(B, H, Lq, Lk, d, "bf16", 5500 + seed)
+    o, l = run_gpu(q, k, v, "bf16", causal, kl)
+    ro, rl = oracle_ref(q, k, v, "bf16", causal, kl)
+    assert_close(o, l, ro, rl, "bf16", what)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_random_forward_f32(seed):
     rng = np.random.default_rng(6000 + seed)
