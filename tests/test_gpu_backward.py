@@ -132,6 +132,9 @@ CASES = [
     # per compute unit: the kernels renumber their units in compute-unit pairs
     (2, 80, 256, 256, True, None),
     (1, 135, 256, 256, True, None),
+    # causal, a few more blocks than resident workgroups: single items
+    # rather than long/short pairs
+    (1, 129, 512, 512, True, None),
 ]
 
 

@@ -52,6 +52,12 @@ CASES = [
     # the plain order)
     (3, 91, 100, 320, False, [320, 7, 200]),
     (1, 135, 256, 256, True, None),
+    # causal, a few more items than resident workgroups: single items
+    # rather than long/short pairs (pairs would leave slots idle), once
+    # with up to 1.6 slots' worth of items and once with short items whose
+    # pairs would end in a round under 60% full
+    (1, 129, 512, 512, True, None),
+    (2, 300, 256, 256, True, None),
 ]
 
 
@@ -144,3 +150,38 @@ def test_tile_names_and_refusals():
         kk = torch.empty((B, H, Lk, d), dtype=torch.bfloat16, device="meta")
         name = sdpa.binding.sdpa_kernel_name(sdpa.binding.handle_for(1, 0), B, H, Lq, Lk, d, causal, False)
         assert name in TILES[d], name
+
+
+# One shape per rule of the tile selector (B, H, Lq, Lk, d_k, causal, key
+# lengths given) and the tile it picks on a 256-CU MI355X.
+SELECTOR_CASES = [
+    ((4, 96, 4096, 4096, 128, True, False), "bf16_d128_bc64_w4"),        # many items
+    ((1, 8, 4096, 4096, 128, True, False), "bf16_d128_bc64_w4_ks2"),     # <= 1 item per CU, long keys
+    ((2, 16, 1024, 1024, 128, False, False), "bf16_d128_bc64_w4_ks2"),
+    ((4, 16, 512, 512, 128, True, False), "bf16_d128_bc64_w4"),          # 8 key tiles: too short to split
+    ((2, 40, 512, 512, 128, False, False), "bf16_d128_bc64_w8"),         # 1..2 items per CU, whole blocks
+    ((32, 3, 302, 302, 128, False, False), "bf16_d128_bc64_w4"),         # same, but 256-row blocks waste rows
+    ((1, 10, 8192, 8192, 128, True, False), "bf16_d128_bc64_w8"),        # 2.5 items per CU, long keys
+    ((8, 8, 1024, 1024, 128, True, True), "bf16_d128_bc64_w4"),          # key lengths: no w8
+    ((4, 32, 1024, 1024, 128, False, True), "bf16_d128_bc64_w4_pairs"),  # key lengths, > 2 items per CU
+    ((8, 8, 512, 2048, 64, False, True), "bf16_d64_bc64_w4_ks2"),        # key lengths, <= 1 item per CU
+    ((64, 8, 128, 128, 64, False, False), "bf16_d64_bc64_w4"),           # encoder workload
+    ((32, 8, 256, 256, 64, True, False), "bf16_d64_bc64_w4"),            # decoder workload
+    ((32, 8, 256, 512, 64, False, True), "bf16_d64_bc64_w4"),            # cross-attention workload
+    ((1, 8, 8192, 8192, 64, True, False), "bf16_d64_bc64_w4_ks2"),       # causal, >= 32 key tiles
+    ((16, 4, 1536, 1536, 64, True, False), "bf16_d64_bc64_w8"),          # causal, 3 items per CU
+    ((16, 2, 6600, 6600, 64, False, False), "bf16_d64_bc64_w4_ks2"),     # 6.5 items per CU, long keys
+    ((64, 16, 512, 512, 64, False, False), "bf16_d64_bc64_w8"),          # many items, whole blocks
+]
+
+
+@pytest.mark.parametrize("case,expected", SELECTOR_CASES, ids=[e for _, e in SELECTOR_CASES])
+def test_selector_choices(case, expected):
+    require_gpu()
+    import torch
+    import transformer_scaled_dot_sdpa_amd as sdpa
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the table is for a 256-CU device")
+    B, H, Lq, Lk, d, causal, lens = case
+    name = sdpa.binding.sdpa_kernel_name(sdpa.binding.handle_for(1, 0), B, H, Lq, Lk, d, causal, lens)
+    assert name == expected, (case, name)

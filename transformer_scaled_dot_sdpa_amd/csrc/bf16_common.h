@@ -136,14 +136,13 @@ __device__ __forceinline__ void map_workgroup(int num_qb, int* bh, int* qb) {
     *qb = CAUSAL ? num_qb - 1 - q : q;
 }
 
-// Units of work for this workgroup: first, first + step, ... below last.
-// The grid is sized to the workgroups the GPU holds at once, and every
-// workgroup stays resident until all its units are done.  Workgroup ids are
-// dealt to the 8 XCDs in turn; each XCD gets a contiguous share of the units
-// (proportional to its workgroups) and its workgroups take those units
-// round-robin, so the workgroups running side by side on one XCD work on
-// neighbouring units -- the query blocks of a few heads, whose K and V then
-// stay in that XCD's L2.
+// Units of work for this workgroup: first, first + step, ... below last
+// (the launches here size the grid to one workgroup per unit, so each
+// workgroup gets exactly one).  Workgroup ids are dealt to the 8 XCDs in
+// turn; each XCD gets a contiguous share of the units (proportional to its
+// workgroups) and its workgroups take those units round-robin, so the
+// workgroups running side by side on one XCD work on neighbouring units --
+// the query blocks of a few heads, whose K and V then stay in that XCD's L2.
 __device__ __forceinline__ void workgroup_units(int num_units, int* first, int* step, int* last) {
     const int nwg = gridDim.x;
     const int g = blockIdx.x;
@@ -180,6 +179,23 @@ __device__ __forceinline__ int cu_pair_unit(int num_units, int cus_per_xcd, int 
     const int P = R - C;
     const int local = j < P ? 2 * j : (j >= C ? 2 * (j - C) + 1 : 2 * P + (j - P));
     return ulo + local;
+}
+
+// Work items per scheduling unit for causal problems (host side).  Query
+// (or key) blocks of a slice alternate long and short, so once the items
+// outnumber the resident slots a unit of two consecutive items -- a long and
+// a short one -- makes every unit equally long.  But pairs halve the number
+// of units, and where that leaves slots idle single items under dynamic
+// dispatch finish sooner: up to single_max items (pairs would fill only
+// part of the slots), and, when short_steps > 0, for items of at most
+// short_steps key tiles whose pairs would end in a round at most 60% full
+// (short items even out by themselves).  steps: key tiles of 64 in the
+// longest item.
+inline int causal_items_per_unit(long long items, long long slots, long long single_max, int steps,
+                                 int short_steps) {
+    if (items <= slots || items <= single_max) return 1;
+    const long long last = ((items + 1) / 2) % slots;   // pairs in their last round
+    return (steps <= short_steps && last > 0 && 5 * last <= 3 * slots) ? 1 : 2;
 }
 
 // Work item -> (b*H + h, query block).  Causal query blocks of a head are

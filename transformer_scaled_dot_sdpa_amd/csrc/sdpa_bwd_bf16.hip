@@ -600,13 +600,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
 
     // causal work runs as long/short pairs of items once the items
-    // outnumber the resident workgroups (2 per CU); a smaller problem takes
-    // one item per workgroup so that every item starts at once, renumbered
-    // so that a compute unit holding two runs a long and a short one
-    // (cu_pair_unit; the query or key blocks of a slice alternate long and
-    // short, and an even count keeps the alternation aligned)
+    // outnumber the resident workgroups (2 per CU), except below 1.25 slots'
+    // worth of items, where pairs would leave slots idle
+    // (causal_items_per_unit); a smaller problem takes one item per
+    // workgroup so that every item starts at once, renumbered so that a
+    // compute unit holding two runs a long and a short one (cu_pair_unit;
+    // the query or key blocks of a slice alternate long and short, and an
+    // even count keeps the alternation aligned)
     const int cus = a.num_cus > 0 ? a.num_cus : 256;
     const long long slots = (long long)cus * 2;
+    const long long single_max = (5 * slots - 1) / 4;
     auto cu_pairs_for = [&](long long items) {
         return (CAUSAL && p.upi == 1 && items <= slots && items > cus && p.num_blocks % 2 == 0 && cus % 8 == 0)
                    ? cus / 8 : 0;
@@ -616,7 +619,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         const long long items = (long long)p.num_blocks * a.B * a.H;
         if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         p.num_items = (int)items;
-        p.upi = (CAUSAL && items > slots) ? 2 : 1;
+        p.upi = CAUSAL ? causal_items_per_unit(items, slots, single_max, 0, 0) : 1;
         p.num_units = (int)((items + p.upi - 1) / p.upi);
         p.cu_pairs = cu_pairs_for(items);
         hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, LENS>), dim3((unsigned)p.num_units), dim3(256), 0,
@@ -629,7 +632,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         const long long items = (long long)p.num_blocks * a.B * a.H;
         if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         p.num_items = (int)items;
-        p.upi = (CAUSAL && items > slots) ? 2 : 1;
+        p.upi = CAUSAL ? causal_items_per_unit(items, slots, single_max, 0, 0) : 1;
         p.num_units = (int)((items + p.upi - 1) / p.upi);
         p.cu_pairs = cu_pairs_for(items);
         if constexpr (kSplitDkDv<D>) {

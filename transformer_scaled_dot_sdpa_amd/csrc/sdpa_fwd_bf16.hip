@@ -658,10 +658,14 @@ hipError_t launch_one(const FwdArgs& a, int sched, hipStream_t stream) {
     // one unit per workgroup: the hardware hands units to free slots as they
     // come, which balances better than a fixed assignment.  Causal units are
     // long/short pairs of equal length once there are more items than
-    // resident workgroups; a smaller problem takes one item per workgroup so
-    // that every item starts at once.
+    // resident workgroups, unless pairs would leave slots idle
+    // (causal_items_per_unit: with two workgroups per CU up to 1.6 slots'
+    // worth of items, and items of at most 8 key tiles); a smaller problem
+    // takes one item per workgroup so that every item starts at once.
     const long long slots = (long long)(a.num_cus > 0 ? a.num_cus : 256) * fwd_blocks_per_cu<D, NW, KS>();
-    p.upi = (CAUSAL && items > slots) ? 2 : 1;
+    p.upi = CAUSAL ? causal_items_per_unit(items, slots, fwd_blocks_per_cu<D, NW, KS>() == 2 ? 8 * slots / 5 : slots,
+                                           ((a.Lq < a.Lk ? a.Lq : a.Lk) + 63) / 64, 8)
+                   : 1;
     p.B = a.B;
     // Compute-unit pairs (default schedule): when every workgroup is
     // resident at once and some compute units hold two, renumber the units

@@ -9,6 +9,8 @@
 //   cus    = compute units; the default tile keeps 2 workgroups per CU
 //   steps  = key tiles of 64 in a row's longest range (Lk; for causal,
 //            min(Lq, Lk))
+//   whole  = the 256-row blocks of the 8-wavefront tile cover no more rows
+//            than the 128-row blocks (B*H*ceil(Lq/256) * 2 == items)
 //
 //   bf16_d*_bc64_w4       default: 4 wavefronts (128 rows) per workgroup,
 //                         2 per CU; the only tile with d_v != d_k and masks.
@@ -19,27 +21,33 @@
 //                         ranked key lengths alike.
 //   bf16_d*_bc64_w4_ks2   two groups of 4 wavefronts take alternate key
 //                         tiles of the same 128 rows: half the tile steps
-//                         per item.  d128: 1 workgroup per CU; wins with at
-//                         most one item per CU and long key ranges (>= 32
-//                         steps causal, >= 16 otherwise).  d64: 4 wavefronts
-//                         per SIMD (128 registers), 2 workgroups per CU;
-//                         wins with at most one item per CU and >= 16 steps,
-//                         or causal with at most two and >= 32 steps.
-//   bf16_d*_bc64_w8       8 wavefronts (256 rows) share each K/V tile:
-//                         half the L2->LDS bytes per flop.  d128: 1
-//                         workgroup per CU; d64: four wavefronts per SIMD,
-//                         2 workgroups per CU.  Wins with no key lengths for
-//                         2..4 items per CU (causal: above 2) with >= 16
-//                         steps (d64: at most 64 steps, and >= 32 above 2
-//                         items per CU), and at d64 from 4 items per CU on.
+//                         per item (d128: 1 workgroup per CU; d64: 4
+//                         wavefronts per SIMD, 2 workgroups per CU).  Wins
+//                         with at most one item per CU and long enough key
+//                         ranges (d128: >= 10 steps causal, >= 16 otherwise;
+//                         d64: >= 9 causal, >= 12 otherwise, >= 16 with key
+//                         lengths), and at d64 also with more items: causal
+//                         from 32 steps, non-causal from 24 steps up to 6.5
+//                         items per CU.
+//   bf16_d*_bc64_w8       8 wavefronts (256 rows) share each K/V tile: half
+//                         the L2->LDS bytes per flop (d128: 1 workgroup per
+//                         CU; d64: 4 wavefronts per SIMD, 2 workgroups per
+//                         CU).  Only without key lengths and with whole
+//                         256-row blocks where rows would be wasted, it wins
+//                         at d128 non-causal with 1..2 items per CU, at d128
+//                         causal with 2.4..4 items per CU and >= 30 steps, at
+//                         d64 causal with 3..4.2 items per CU, and at d64
+//                         non-causal from 2 items per CU (where the key split
+//                         does not).
 //   bf16_d*_bc64_w4_pairs per-batch key lengths, no causal mask: batches
 //                         ranked by length, each workgroup runs the i-th
-//                         longest and the i-th shortest item.  Wins when the
-//                         items need between two and four rounds of slots.
+//                         longest and the i-th shortest item.  Wins with more
+//                         than 2 items per CU and >= 16 steps.
 //
-// The thresholds come from timing every tile on 42 shapes on MI355X
-// (interleaved batches, median of 3); the design notes list the table.  On
-// all of them the choice is within 2% of the fastest tile.
+// The thresholds come from timing every tile on MI355X (interleaved batches,
+// median of 3) on 43 chosen shapes and 320 shapes drawn at random; the
+// design notes list the tables and the check on further random shapes that
+// none of the thresholds was fitted to.
 #include <string.h>
 
 #include "sdpa_internal.h"
@@ -80,21 +88,30 @@ bool select_bf16_tile(int d, int causal, int has_key_lens, long long bh, int Lq,
     if (d != 64 && d != 128) return false;
     const long long cus = num_cus > 0 ? num_cus : 256;
     const long long items = bh * ((Lq + 127) / 128);
+    const bool whole = 2 * (bh * ((Lq + 255) / 256)) == items;
     const long long steps = ((causal ? (Lq < Lk ? Lq : Lk) : Lk) + 63) / 64;
-    const char* name = d == 128 ? "bf16_d128_bc64_w4" : "bf16_d64_bc64_w4";
-    if (has_key_lens && !causal && items > 2 * cus && items <= 4 * cus) {
-        name = d == 128 ? "bf16_d128_bc64_w4_pairs" : "bf16_d64_bc64_w4_pairs";
-    } else if (!general && d == 128 && items <= cus && steps >= (causal ? 32 : 16)) {
-        name = "bf16_d128_bc64_w4_ks2";
-    } else if (!general && d == 64 && (causal ? items <= 2 * cus && steps >= 32 : items <= cus && steps >= 16)) {
-        name = "bf16_d64_bc64_w4_ks2";
-    } else if (!general && !has_key_lens &&
-               (((causal ? items > 2 * cus : items >= 2 * cus) && items <= 4 * cus && steps >= 16 &&
-                 (d == 128 || (steps <= 64 && (items <= 2 * cus || steps >= 32)))) ||
-                (d == 64 && items >= 4 * cus))) {
-        name = d == 128 ? "bf16_d128_bc64_w8" : "bf16_d64_bc64_w8";
+    const bool lens = has_key_lens != 0;
+    enum { W4, PAIRS, KS2, W8 } t = W4;
+    if (lens && !causal) {
+        if (items > 2 * cus && steps >= 16) t = PAIRS;
+        else if (items <= cus && steps >= 16) t = KS2;
+    } else if (d == 128) {
+        if (items <= cus && steps >= (causal ? 10 : 16)) t = KS2;
+        else if (!lens && whole && !causal && items > cus && items <= 2 * cus) t = W8;
+        else if (!lens && causal && 5 * items >= 12 * cus && items <= 4 * cus && steps >= 30) t = W8;
+    } else if (causal) {
+        if ((items <= cus && steps >= 9) || steps >= 32) t = KS2;
+        else if (!lens && whole && items >= 3 * cus && 5 * items <= 21 * cus) t = W8;
+    } else {
+        if ((items <= cus && steps >= 12) || (steps >= 24 && 2 * items <= 13 * cus)) t = KS2;
+        else if (!lens && whole && items > 2 * cus) t = W8;
     }
-    *out = *tile_named(d, name);
+    // d_v != d_k and additive masks run in the default geometry only
+    if (general && t != PAIRS) t = W4;
+    static const char* const kNames[2][4] = {
+        {"bf16_d64_bc64_w4", "bf16_d64_bc64_w4_pairs", "bf16_d64_bc64_w4_ks2", "bf16_d64_bc64_w8"},
+        {"bf16_d128_bc64_w4", "bf16_d128_bc64_w4_pairs", "bf16_d128_bc64_w4_ks2", "bf16_d128_bc64_w8"}};
+    *out = *tile_named(d, kNames[d == 128][t]);
     return true;
 }
 

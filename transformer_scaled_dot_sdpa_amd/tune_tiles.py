@@ -11,6 +11,11 @@ batches of back-to-back calls between two HIP events (enough calls for about
 the median per tile is reported, with the tile the selector picks
 (``sdpa_kernel_name``) and its distance to the fastest.  Input sets are
 rotated so that a shape's inputs exceed the 256 MiB Infinity Cache.
+
+    python -m transformer_scaled_dot_sdpa_amd.tune_tiles --random 40 --seed 7
+
+times shapes drawn at random instead (held out: none of them was used to set
+the thresholds), to check that the selector generalises.
 """
 from __future__ import annotations
 
@@ -41,6 +46,36 @@ SHAPES = [
     (64, 32, 16, 1024, 1024, True, None), (64, 64, 16, 512, 512, False, None), (64, 4, 32, 2048, 2048, False, None),
 ]
 QUICK = [SHAPES[i] for i in (0, 1, 2, 18, 19, 22, 28)]
+
+
+def random_shapes(n, seed, cus=256):
+    """n shapes drawn from a seeded distribution over the selector's inputs:
+    d_k 64 or 128, causal or not, key lengths in 40% of the non-causal
+    draws, sequence lengths 100-8192 (cross-attention key ranges up to 4x
+    the queries), and B·H such that the query blocks number between 1/4 and
+    16 per compute unit (log-uniform).  Work is capped at about 2 TFLOP per
+    call so that every shape times in well under a second."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(rng.choice([64, 128]))
+        causal = bool(rng.random() < 0.5)
+        Lq = int(round(float(np.exp(rng.uniform(np.log(100), np.log(8192))))))
+        Lk = Lq if causal or rng.random() < 0.5 else int(min(8192, round(Lq * float(rng.uniform(0.5, 4.0)))))
+        nqb = (Lq + 127) // 128
+        items = float(np.exp(rng.uniform(np.log(cus / 4), np.log(16 * cus))))
+        bh = max(1, int(round(items / nqb)))
+        B = int(rng.choice([b for b in (1, 2, 4, 8, 16, 32) if b <= bh] or [1]))
+        H = max(1, int(round(bh / B)))
+        kl = None
+        if not causal and rng.random() < 0.4 and B > 1:
+            lo = int(rng.integers(1, max(2, Lk // 2)))
+            kl = (lo, Lk)
+        if 4.0 * B * H * Lq * Lk * d / (2 if causal else 1) > 2e12:
+            continue
+        out.append((d, B, H, Lq, Lk, causal, kl))
+    return out
 
 
 def time_shape(torch, sdpa, d, B, H, Lq, Lk, causal, kl, rounds=3):
@@ -91,6 +126,8 @@ def time_shape(torch, sdpa, d, B, H, Lq, Lk, causal, kl, rounds=3):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--quick", action="store_true", help="seven shapes only")
+    ap.add_argument("--random", type=int, default=0, metavar="N", help="N random (held-out) shapes instead")
+    ap.add_argument("--seed", type=int, default=7, help="seed of the random shapes")
     args = ap.parse_args()
     import torch
     import transformer_scaled_dot_sdpa_amd as sdpa
@@ -100,7 +137,8 @@ def main():
           + " | ".join(t.split("_", 2)[2] for t in TILES[128]) + " | chosen, µs |")
     print("|---|---|---|---|---|---|---|" + "---|" * len(TILES[128]) + "---|")
     off = []
-    for (d, B, H, Lq, Lk, causal, kl) in (QUICK if args.quick else SHAPES):
+    shapes = random_shapes(args.random, args.seed, cus) if args.random else (QUICK if args.quick else SHAPES)
+    for (d, B, H, Lq, Lk, causal, kl) in shapes:
         res, chosen = time_shape(torch, sdpa, d, B, H, Lq, Lk, causal, kl)
         items = B * H * ((Lq + 127) // 128)
         steps = ((min(Lq, Lk) if causal else Lk) + 63) // 64
@@ -114,8 +152,9 @@ def main():
         print(f"| {d} | {B}·{H} | {Lq} × {Lk} | {'yes' if causal else 'no'} | {klt} | {items / cus:.3g} | {steps} | "
               + " | ".join(cells) + f" | {chosen.split('_', 2)[2]} {res[chosen]:.1f}{mark} |", flush=True)
     within = sum(r < 0.02 for r in off)
-    print(f"\nThe choice is within 2% of the fastest tile on {within} of {len(off)} shapes "
-          f"(worst {100 * max(off):.1f}% off).", flush=True)
+    print(f"\nThe choice is within 2% of the fastest tile on {within} of {len(off)} shapes, "
+          f"within 5% on {sum(r < 0.05 for r in off)} (worst {100 * max(off):.1f}% off, "
+          f"mean {100 * sum(off) / len(off):.2f}%).", flush=True)
 
 
 if __name__ == "__main__":
