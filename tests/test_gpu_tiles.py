@@ -159,6 +159,8 @@ SELECTOR_CASES = [
     ((1, 8, 4096, 4096, 128, True, False), "bf16_d128_bc64_w4_ks2"),     # <= 1 item per CU, long keys
     ((2, 16, 1024, 1024, 128, False, False), "bf16_d128_bc64_w4_ks2"),
     ((4, 16, 512, 512, 128, True, False), "bf16_d128_bc64_w4"),          # 8 key tiles: too short to split
+    ((2, 13, 2048, 2048, 128, True, False), "bf16_d128_bc64_w4_ks2"),    # causal, 1..2 items per CU, even blocks
+    ((8, 2, 2066, 2066, 128, True, False), "bf16_d128_bc64_w4"),         # same, odd blocks per slice
     ((2, 40, 512, 512, 128, False, False), "bf16_d128_bc64_w8"),         # 1..2 items per CU, whole blocks
     ((32, 3, 302, 302, 128, False, False), "bf16_d128_bc64_w4"),         # same, but 256-row blocks waste rows
     ((1, 10, 8192, 8192, 128, True, False), "bf16_d128_bc64_w8"),        # 2.5 items per CU, long keys
@@ -169,6 +171,7 @@ SELECTOR_CASES = [
     ((32, 8, 256, 256, 64, True, False), "bf16_d64_bc64_w4"),            # decoder workload
     ((32, 8, 256, 512, 64, False, True), "bf16_d64_bc64_w4"),            # cross-attention workload
     ((1, 8, 8192, 8192, 64, True, False), "bf16_d64_bc64_w4_ks2"),       # causal, >= 32 key tiles
+    ((8, 4, 1280, 1280, 64, True, False), "bf16_d64_bc64_w4_ks2"),       # causal, <= 2 items per CU, 20 tiles
     ((16, 4, 1536, 1536, 64, True, False), "bf16_d64_bc64_w8"),          # causal, 3 items per CU
     ((16, 2, 6600, 6600, 64, False, False), "bf16_d64_bc64_w4_ks2"),     # 6.5 items per CU, long keys
     ((64, 16, 512, 512, 64, False, False), "bf16_d64_bc64_w8"),          # many items, whole blocks

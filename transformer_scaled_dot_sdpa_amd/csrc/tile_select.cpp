@@ -26,9 +26,11 @@
 //                         with at most one item per CU and long enough key
 //                         ranges (d128: >= 10 steps causal, >= 16 otherwise;
 //                         d64: >= 9 causal, >= 12 otherwise, >= 16 with key
-//                         lengths), and at d64 also with more items: causal
-//                         from 32 steps, non-causal from 24 steps up to 6.5
-//                         items per CU.
+//                         lengths), causal with up to two items per CU from
+//                         32 steps (d128, an even number of query blocks
+//                         per slice) or 20 steps (d64), and at d64 also with
+//                         more items: causal from 32 steps, non-causal from
+//                         24 steps up to 6.5 items per CU.
 //   bf16_d*_bc64_w8       8 wavefronts (256 rows) share each K/V tile: half
 //                         the L2->LDS bytes per flop (d128: 1 workgroup per
 //                         CU; d64: 4 wavefronts per SIMD, 2 workgroups per
@@ -45,9 +47,10 @@
 //                         than 2 items per CU and >= 16 steps.
 //
 // The thresholds come from timing every tile on MI355X (interleaved batches,
-// median of 3) on 43 chosen shapes and 320 shapes drawn at random; the
-// design notes list the tables and the check on further random shapes that
-// none of the thresholds was fitted to.
+// median of 3) on 43 chosen shapes, 320 shapes drawn at random and a grid of
+// causal shapes around the key-split boundaries; the design notes list the
+// tables and the check on further random shapes that none of the
+// thresholds was fitted to.
 #include <string.h>
 
 #include "sdpa_internal.h"
@@ -97,10 +100,14 @@ bool select_bf16_tile(int d, int causal, int has_key_lens, long long bh, int Lq,
         else if (items <= cus && steps >= 16) t = KS2;
     } else if (d == 128) {
         if (items <= cus && steps >= (causal ? 10 : 16)) t = KS2;
+        // up to two items per CU the split's single workgroup per CU runs
+        // long/short pairs, balanced only when a slice has an even number
+        // of query blocks (pairs do not then straddle two slices)
+        else if (causal && items <= 2 * cus && steps >= 32 && ((Lq + 127) / 128) % 2 == 0) t = KS2;
         else if (!lens && whole && !causal && items > cus && items <= 2 * cus) t = W8;
         else if (!lens && causal && 5 * items >= 12 * cus && items <= 4 * cus && steps >= 30) t = W8;
     } else if (causal) {
-        if ((items <= cus && steps >= 9) || steps >= 32) t = KS2;
+        if ((items <= cus && steps >= 9) || (items <= 2 * cus && steps >= 20) || steps >= 32) t = KS2;
         else if (!lens && whole && items >= 3 * cus && 5 * items <= 21 * cus) t = W8;
     } else {
         if ((items <= cus && steps >= 12) || (steps >= 24 && 2 * items <= 13 * cus)) t = KS2;
