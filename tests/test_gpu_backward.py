@@ -135,6 +135,9 @@ CASES = [
     # causal, a few more blocks than resident workgroups: single items
     # rather than long/short pairs
     (1, 129, 512, 512, True, None),
+    # causal pairs with an odd number of blocks per slice (units of two
+    # items then span two slices)
+    (2, 150, 300, 300, True, None),
 ]
 
 

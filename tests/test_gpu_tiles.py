@@ -58,6 +58,9 @@ CASES = [
     # pairs would end in a round under 60% full
     (1, 129, 512, 512, True, None),
     (2, 300, 256, 256, True, None),
+    # causal long/short pairs with an odd number of query blocks per slice
+    # (units of two items then span two slices)
+    (2, 150, 300, 300, True, None),
 ]
 
 
