@@ -96,6 +96,52 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t nby
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// A wavefront's 32 x W block of results in the 32x32x16 accumulator layout
+// (lane n + 32h, column tile t, register r: row n, column 32t + 8(r/4) +
+// 4h + r%4), times the lane's `mul`, rounded to bf16 and stored as whole
+// rows.  Stored straight from the accumulators, every instruction would
+// write 8 bytes of each of 32 rows: partial cache lines.  Instead the block
+// goes to `stage` (32*W elements of LDS, row-major, the 16-byte chunks of a
+// row XOR-swizzled by the row so that the 32 rows' writes spread over the
+// banks) and is read back so that consecutive lanes hold consecutive 16
+// bytes of one row; 16-byte non-temporal stores then write whole lines:
+// rows i < rows of the block go to dst + i * ld.  The caller makes sure no
+// other wavefront still reads `stage`.
+template <int W>
+__device__ __forceinline__ void store_rows_bf16(const f32x16* acc, float mul, lds_u16* stage, uint16_t* dst,
+                                                size_t ld, int rows, int lane) {
+    constexpr int CPR = W / 8;     // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;  // rows per store instruction
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    // the empty asm keeps the compiler from computing the lane's LDS offsets
+    // once at kernel start and holding them in registers through the loops
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int n = ln & 31, h = ln >> 5;
+#pragma unroll
+    for (int t = 0; t < W / 32; ++t)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            __bf16 w[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w[c] = (__bf16)(acc[t][4 * g4 + c] * mul);
+            const int ch = (4 * t + g4) ^ (n & (CPR - 1));
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stage + n * W + ch * 8 + 4 * h) =
+                __builtin_bit_cast(u32x2, w);
+        }
+    const int r_in = ln / CPR, c = ln % CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int row = i * RPI + r_in;
+        const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            stage + row * W + ((c ^ (row & (CPR - 1))) * 8));
+        if (row < rows) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + (size_t)row * ld + c * 8));
+    }
+}
+
 // x combined with its value in lane l ^ 32.  v_permlane32_swap(a, b)
 // returns (a[l], a[l + 32]) in lanes l < 32 and (b[l - 32], b[l]) in lanes
 // l >= 32, so with a = b = x each lane gets its own value and its partner's.

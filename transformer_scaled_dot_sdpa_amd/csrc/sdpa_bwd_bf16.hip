@@ -300,20 +300,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BParams p) {
         }
     }
 
-    // dQ = (dS K) / sqrt(d): accumulator r of column tile dt is feature
-    // dt*32 + 8*(r/4) + 4h + r%4 of row qrow
-    if (row_ok) {
-        uint16_t* dst = p.dq + q_base + (size_t)qrow * D;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                __bf16 w[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) w[c] = (__bf16)(acc[dt][4 * g4 + c] * p.scale);
-                *reinterpret_cast<uint2*>(dst + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, w);
-            }
-    }
+    // dQ = (dS K) / sqrt(d), stored as whole rows through the K buffers
+    // (two wavefronts' 32 x D blocks each), free once every wavefront has
+    // passed the barrier
+    __syncthreads();
+    store_rows_bf16<D>(acc, p.scale, (lds_u16*)((wave >> 1) ? k_lds1 : k_lds0) + (wave & 1) * 32 * D,
+                       p.dq + q_base + (size_t)q0w * D, D, p.Lq - q0w, lane);
     __syncthreads();
     }
 }
@@ -554,27 +546,16 @@ __global__ void __launch_bounds__(256, MODE == 0 ? 1 : 2) bwd_dkdv_kernel(BParam
         }
     }
 
-    // dK = dS^T Q / sqrt(d), dV = P^T dO: accumulator r of column tile dt is
-    // feature dt*32 + 8*(r/4) + 4h + r%4 of key `key`
-    if (key < p.Lk) {
-        uint16_t* dstk = p.dk + kv_base + (size_t)key * D;
-        uint16_t* dstv = p.dv + kv_base + (size_t)key * D;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                __bf16 wk[4], wv[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    wk[c] = (__bf16)(dka[dt][4 * g4 + c] * p.scale);
-                    wv[c] = (__bf16)dva[dt][4 * g4 + c];
-                }
-                if constexpr (DO_DK)
-                    *reinterpret_cast<uint2*>(dstk + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wk);
-                if constexpr (DO_DV)
-                    *reinterpret_cast<uint2*>(dstv + dt * 32 + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, wv);
-            }
-    }
+    // dK = dS^T Q / sqrt(d) and dV = P^T dO, stored as whole rows (keys)
+    // through the Q buffers (dK) and the dO buffers (dV), two wavefronts'
+    // 32 x D blocks each, free once every wavefront has passed the barrier
+    __syncthreads();
+    if constexpr (DO_DK)
+        store_rows_bf16<D>(dka, p.scale, (lds_u16*)((wave >> 1) ? q_lds1 : q_lds0) + (wave & 1) * 32 * D,
+                           p.dk + kv_base + (size_t)k0w * D, D, p.Lk - k0w, lane);
+    if constexpr (DO_DV)
+        store_rows_bf16<D>(dva, 1.f, (lds_u16*)((wave >> 1) ? g_lds1 : g_lds0) + (wave & 1) * 32 * D,
+                           p.dv + kv_base + (size_t)k0w * D, D, p.Lk - k0w, lane);
     __syncthreads();
     }
 }

@@ -598,17 +598,12 @@ fwd_bf16_kernel(KParams p) {
         }
     }
 
-    // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l).  A lane holds
-    // 4-column pieces of one row, so stores straight from the accumulators
-    // would write 8 bytes of each of 32 rows per instruction: partial cache
-    // lines.  Instead each wavefront stages its 32 x DV outputs in LDS (the
-    // K/V buffers, free after the barrier below), row-major with the 16-byte
-    // chunks of a row XOR-swizzled by the row so that the 32 rows' writes
-    // spread over the banks, and reads them back so that consecutive lanes
-    // store consecutive 16 bytes of one row: whole lines, written with
-    // non-temporal stores that do not stay in L2.  Measured on MI355X
-    // against the direct stores (same machine, interleaved): encoder_d64
-    // -20%, decoder_causal_d64 -20%, cross_padded_d64 -11%, the large causal
+    // ---- epilogue: O = O^T / l, lse = ln 2 * (m + log2 l).  Each
+    // wavefront stages its 32 output rows in the K/V buffers (free after the
+    // barrier below) and stores whole rows with non-temporal 16-byte stores
+    // (store_rows_bf16).  Measured on MI355X against stores straight from
+    // the accumulators (same machine, interleaved): encoder_d64 -20%,
+    // decoder_causal_d64 -20%, cross_padded_d64 -11%, the large causal
     // workload -2.4%.  The kernels with an additive mask, at the register
     // limit already, keep the direct stores: staged, they ran 3% slower.
     const float l = sum_across_halves(l_run);
@@ -629,40 +624,14 @@ fwd_bf16_kernel(KParams p) {
         }
     } else {
         static_assert(NW <= 4 * KS || D == DV, "staging needs the K buffers");
-        constexpr int CPRO = DV / 8;            // 16-byte chunks per output row
-        constexpr int RPI = 64 / CPRO;          // rows per store instruction
-        constexpr int PER = 2 * KS;             // wavefronts per staging buffer
-        typedef __attribute__((address_space(3))) uint16_t lds_u16;
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        __syncthreads();   // every wavefront is done reading the last K/V tile
+        constexpr int PER = 2 * KS;   // wavefronts per staging buffer (32 rows x DV each)
+        __syncthreads();              // every wavefront is done reading the last K/V tile
         if (grp == 0) {
             const int bi = wave / PER;
             lds_u16* stage = (lds_u16*)(bi == 0 ? v_lds0 : bi == 1 ? v_lds1 : bi == 2 ? k_lds0 : k_lds1) +
                              (wave % PER) * 32 * DV;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    __bf16 w[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) w[c] = (__bf16)(o[dt][4 * g4 + c] * inv);
-                    // accumulator r of column tile dt: column dt*32 + 8*(r/4) + 4h + r%4
-                    const int ch = (dt * 4 + g4) ^ (n & (CPRO - 1));
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stage + n * DV + ch * 8 + 4 * h) =
-                        __builtin_bit_cast(u32x2, w);
-                }
-            const int r_in = lane / CPRO, c = lane % CPRO;
-            uint16_t* obase = p.out + b * p.o_sb + hh * p.o_sh;
-#pragma unroll
-            for (int i = 0; i < 32 / RPI; ++i) {
-                const int row = i * RPI + r_in;
-                const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                    stage + row * DV + ((c ^ (row & (CPRO - 1))) * 8));
-                if (q0w + row < p.Lq)
-                    __builtin_nontemporal_store(
-                        v, reinterpret_cast<u32x4*>(obase + (size_t)(q0w + row) * p.o_sl + c * 8));
-            }
+            store_rows_bf16<DV>(o, inv, stage, p.out + b * p.o_sb + hh * p.o_sh + (size_t)q0w * p.o_sl,
+                                (size_t)p.o_sl, p.Lq - q0w, lane);
         }
     }
     if (grp == 0 && qrow < p.Lq && p.lse != nullptr && h == 0)
