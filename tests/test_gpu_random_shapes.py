@@ -100,6 +100,24 @@ def test_random_backward_bf16(seed):
     check_case(B, H, Lq, Lk, d, "bf16", causal, kl, 7000 + seed, f"random bf16 seed={seed} d{d}")
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_random_backward_bf16_many_items(seed):
+    """About 200 to 1100 query (and key) blocks, i.e. up to four per CU:
+    the backward's schedules for causal problems (one block per workgroup
+    with compute-unit pairing, single blocks just past one round, long/short
+    pairs beyond) and its whole-row result stores at scale."""
+    rng = np.random.default_rng(7200 + seed)
+    d = int(rng.choice([64, 128]))
+    L = int(rng.integers(64, 513))
+    causal = bool(rng.random() < 0.6)
+    B = int(rng.integers(1, 9))
+    target = int(rng.integers(200, 1101))
+    H = max(1, round(target / (B * ((L + 127) // 128))))
+    kl = _key_lens(rng, B, L)
+    check_case(B, H, L, L, d, "bf16", causal, kl, 7200 + seed,
+               f"random bf16 backward (many items) seed={seed} B{B} H{H} L{L} d{d} causal={causal}")
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_random_backward_f32(seed):
     rng = np.random.default_rng(7500 + seed)
