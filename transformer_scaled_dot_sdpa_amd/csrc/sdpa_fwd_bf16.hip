@@ -602,27 +602,12 @@ fwd_bf16_kernel(KParams p) {
     // wavefront stages its 32 output rows in the K/V buffers (free after the
     // barrier below) and stores whole rows with non-temporal 16-byte stores
     // (store_rows_bf16).  Measured on MI355X against stores straight from
-    // the accumulators (same machine, interleaved): encoder_d64 -20%,
-    // decoder_causal_d64 -20%, cross_padded_d64 -11%, the large causal
-    // workload -2.4%.  The kernels with an additive mask, at the register
-    // limit already, keep the direct stores: staged, they ran 3% slower.
+    // the accumulators (same machine, interleaved): encoder_d64 -12%,
+    // decoder_causal_d64 -19%, cross_padded_d64 -14%, the large causal
+    // workload -2.3%, with a shared additive bias -1.5%.
     const float l = sum_across_halves(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if constexpr (MASK) {
-        if (grp == 0 && qrow < p.Lq) {
-            uint16_t* dst = p.out + b * p.o_sb + hh * p.o_sh + (size_t)qrow * p.o_sl;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int d0 = dt * 32 + 8 * g4 + 4 * h;
-                    __bf16 w[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) w[c] = (__bf16)(o[dt][4 * g4 + c] * inv);
-                    *reinterpret_cast<uint2*>(dst + d0) = __builtin_bit_cast(uint2, w);
-                }
-        }
-    } else {
+    {
         static_assert(NW <= 4 * KS || D == DV, "staging needs the K buffers");
         constexpr int PER = 2 * KS;   // wavefronts per staging buffer (32 rows x DV each)
         __syncthreads();              // every wavefront is done reading the last K/V tile
