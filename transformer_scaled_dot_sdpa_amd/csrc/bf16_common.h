@@ -166,65 +166,43 @@ __device__ __forceinline__ float sum_across_halves(float x) {
     return p0 + p1;
 }
 
-// Hardware hands consecutive workgroup ids to the 8 XCDs in turn; this maps
-// them so that each XCD gets a contiguous range of work items (all query
-// blocks of a head then share that XCD's L2).  Causal: longest query blocks
-// of a head first.  Returns (bh, query block).
-template <bool CAUSAL>
-__device__ __forceinline__ void map_workgroup(int num_qb, int* bh, int* qb) {
-    const int nwg = gridDim.x;
-    const int g = blockIdx.x;
-    const int xcd = g & 7, slot = g >> 3;
-    const int per = nwg >> 3, rem = nwg & 7;
-    const int lin = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
-    *bh = lin / num_qb;
-    int q = lin - *bh * num_qb;
-    *qb = CAUSAL ? num_qb - 1 - q : q;
-}
-
-// Units of work for this workgroup: first, first + step, ... below last
-// (the launches here size the grid to one workgroup per unit, so each
-// workgroup gets exactly one).  Workgroup ids are dealt to the 8 XCDs in
-// turn; each XCD gets a contiguous share of the units (proportional to its
-// workgroups) and its workgroups take those units round-robin, so the
-// workgroups running side by side on one XCD work on neighbouring units --
-// the query blocks of a few heads, whose K and V then stay in that XCD's L2.
-__device__ __forceinline__ void workgroup_units(int num_units, int* first, int* step, int* last) {
+// The unit of work of this workgroup; every launch here sizes its grid to
+// one workgroup per unit.  Workgroup ids are dealt to the 8 XCDs in turn;
+// each XCD gets a contiguous range of units (as many as it has workgroups)
+// and its workgroups take them in order, so the workgroups running side by
+// side on one XCD work on neighbouring units -- the query blocks of a few
+// heads, whose K and V then stay in that XCD's L2.  (32-bit arithmetic only:
+// the general form, units spread over fewer workgroups, took two 64-bit
+// divisions, about 200 scalar instructions at the start of every workgroup.)
+__device__ __forceinline__ int workgroup_unit() {
     const int nwg = gridDim.x;
     const int g = blockIdx.x;
     const int xcd = g & 7, j = g >> 3;
     const int per = nwg >> 3, rem = nwg & 7;
-    const int sx = per + (xcd < rem ? 1 : 0);
-    const int wlo = xcd * per + (xcd < rem ? xcd : rem);
-    const int ulo = (int)((long long)num_units * wlo / nwg);
-    const int uhi = (int)((long long)num_units * (wlo + sx) / nwg);
-    *first = ulo + j;
-    *step = sx;
-    *last = uhi;
+    return xcd * per + (xcd < rem ? xcd : rem) + j;
 }
 
-// With one unit per workgroup and every workgroup resident at once, the
-// hardware hands an XCD's workgroups to its C compute units in turn, so the
-// XCD's j-th and (j + C)-th workgroups share a compute unit.  Units that
-// alternate long and short (causal query blocks) would then put two long
-// ones on every other compute unit.  This renumbering gives local workgroup
-// j < P the unit 2j and workgroup j + C the unit 2j + 1 (P = R - C pairs of an
-// XCD range of R units), so that each compute unit holding two workgroups
-// runs one long and one short unit -- of the same head, which also shares
-// its K/V in L2.  unit_first is the workgroup's unit from workgroup_units.
-__device__ __forceinline__ int cu_pair_unit(int num_units, int cus_per_xcd, int unit_first) {
+// With every workgroup resident at once, the hardware hands an XCD's
+// workgroups to its C compute units in turn, so the XCD's j-th and (j + C)-th
+// workgroups share a compute unit.  Units that alternate long and short
+// (causal query blocks) would then put two long ones on every other compute
+// unit.  This renumbering gives local workgroup j < P the unit 2j and
+// workgroup j + C the unit 2j + 1 (P = R - C pairs of an XCD range of R
+// units), so that each compute unit holding two workgroups runs one long and
+// one short unit -- of the same head, which also shares its K/V in L2.  unit
+// is the workgroup's unit from workgroup_unit.
+__device__ __forceinline__ int cu_pair_unit(int cus_per_xcd, int unit) {
     const int nwg = gridDim.x;
     const int g = blockIdx.x;
     const int xcd = g & 7, j = g >> 3;
     const int per = nwg >> 3, rem = nwg & 7;
-    const int sx = per + (xcd < rem ? 1 : 0);
-    const int wlo = xcd * per + (xcd < rem ? xcd : rem);
-    const int ulo = (int)((long long)num_units * wlo / nwg);
-    const int R = sx, C = cus_per_xcd;
-    if (num_units != nwg || R <= C || R > 2 * C || (ulo & 1)) return unit_first;
+    const int R = per + (xcd < rem ? 1 : 0);
+    const int lo = xcd * per + (xcd < rem ? xcd : rem);
+    const int C = cus_per_xcd;
+    if (R <= C || R > 2 * C || (lo & 1)) return unit;
     const int P = R - C;
     const int local = j < P ? 2 * j : (j >= C ? 2 * (j - C) + 1 : 2 * P + (j - P));
-    return ulo + local;
+    return lo + local;
 }
 
 // Work items per scheduling unit for causal problems (host side).  Query

@@ -160,10 +160,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BParams p) {
     TileOffsets<D> off;
     off.init(lane);
 
-    int unit_first, unit_step, unit_last;
-    workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
-    if (CAUSAL && p.cu_pairs > 0) unit_first = cu_pair_unit(p.num_units, p.cu_pairs, unit_first);
-    for (int unit = unit_first; unit < unit_last; unit += unit_step)
+    int unit = workgroup_unit();
+    if (CAUSAL && p.cu_pairs > 0) unit = cu_pair_unit(p.cu_pairs, unit);
     for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
     int bh, qb;
     item_block<CAUSAL>(item, p.num_blocks, &bh, &qb);
@@ -338,10 +336,8 @@ __global__ void __launch_bounds__(256, MODE == 0 ? 1 : 2) bwd_dkdv_kernel(BParam
     TileOffsets<D> off;
     off.init(lane);
 
-    int unit_first, unit_step, unit_last;
-    workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
-    if (CAUSAL && p.cu_pairs > 0) unit_first = cu_pair_unit(p.num_units, p.cu_pairs, unit_first);
-    for (int unit = unit_first; unit < unit_last; unit += unit_step)
+    int unit = workgroup_unit();
+    if (CAUSAL && p.cu_pairs > 0) unit = cu_pair_unit(p.cu_pairs, unit);
     for (int item = unit * p.upi; item < min(unit * p.upi + p.upi, p.num_items); ++item) {
     int bh, kb;
     item_block<CAUSAL>(item, p.num_blocks, &bh, &kb);

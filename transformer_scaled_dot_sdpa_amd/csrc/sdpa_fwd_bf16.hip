@@ -179,11 +179,9 @@ fwd_bf16_kernel(KParams p) {
     }
 
     // ---- the workgroup's work items, one after the other (see
-    // workgroup_units and item_block for the schedule and the order)
-    int unit_first, unit_step, unit_last;
-    workgroup_units(p.num_units, &unit_first, &unit_step, &unit_last);
-    if (p.cu_pairs > 0) unit_first = cu_pair_unit(p.num_units, p.cu_pairs, unit_first);
-    for (int unit = unit_first; unit < unit_last; unit += unit_step)
+    // workgroup_unit and item_block for the schedule and the order)
+    int unit = workgroup_unit();
+    if (p.cu_pairs > 0) unit = cu_pair_unit(p.cu_pairs, unit);
     for (int k_item = 0; k_item < p.upi; ++k_item) {
     int item;
     if (LENS && p.lens_pairs == 1) {
@@ -215,7 +213,9 @@ fwd_bf16_kernel(KParams p) {
     const int q0 = qb * BR;
 
     int kv_len = p.Lk;
-    if (LENS) {
+    if (LENS && p.lens_pairs) {
+        kv_len = s_len[b];   // already clamped, and in LDS: no second trip to memory
+    } else if (LENS) {
         int L = p.key_lens[b];
         L = L < 0 ? 0 : L;
         kv_len = L < kv_len ? L : kv_len;
