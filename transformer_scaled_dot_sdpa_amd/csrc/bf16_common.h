@@ -166,21 +166,21 @@ __device__ __forceinline__ float sum_across_halves(float x) {
     return p0 + p1;
 }
 
-// The unit of work of this workgroup; every launch here sizes its grid to
-// one workgroup per unit.  Workgroup ids are dealt to the 8 XCDs in turn;
+// The unit of work of workgroup g of nwg; every launch here sizes its grid
+// to one workgroup per unit.  Workgroup ids are dealt to the 8 XCDs in turn;
 // each XCD gets a contiguous range of units (as many as it has workgroups)
 // and its workgroups take them in order, so the workgroups running side by
 // side on one XCD work on neighbouring units -- the query blocks of a few
 // heads, whose K and V then stay in that XCD's L2.  (32-bit arithmetic only:
 // the general form, units spread over fewer workgroups, took two 64-bit
 // divisions, about 200 scalar instructions at the start of every workgroup.)
-__device__ __forceinline__ int workgroup_unit() {
-    const int nwg = gridDim.x;
-    const int g = blockIdx.x;
+// A bijection of [0, nwg); host-callable so that it can be checked there.
+__host__ __device__ __forceinline__ int unit_of_workgroup(int nwg, int g) {
     const int xcd = g & 7, j = g >> 3;
     const int per = nwg >> 3, rem = nwg & 7;
     return xcd * per + (xcd < rem ? xcd : rem) + j;
 }
+__device__ __forceinline__ int workgroup_unit() { return unit_of_workgroup(gridDim.x, blockIdx.x); }
 
 // With every workgroup resident at once, the hardware hands an XCD's
 // workgroups to its C compute units in turn, so the XCD's j-th and (j + C)-th
@@ -190,10 +190,9 @@ __device__ __forceinline__ int workgroup_unit() {
 // workgroup j + C the unit 2j + 1 (P = R - C pairs of an XCD range of R
 // units), so that each compute unit holding two workgroups runs one long and
 // one short unit -- of the same head, which also shares its K/V in L2.  unit
-// is the workgroup's unit from workgroup_unit.
-__device__ __forceinline__ int cu_pair_unit(int cus_per_xcd, int unit) {
-    const int nwg = gridDim.x;
-    const int g = blockIdx.x;
+// is workgroup g's unit from unit_of_workgroup; the result is again a
+// bijection of [0, nwg).
+__host__ __device__ __forceinline__ int cu_pair_renumber(int nwg, int g, int cus_per_xcd, int unit) {
     const int xcd = g & 7, j = g >> 3;
     const int per = nwg >> 3, rem = nwg & 7;
     const int R = per + (xcd < rem ? 1 : 0);
@@ -203,6 +202,9 @@ __device__ __forceinline__ int cu_pair_unit(int cus_per_xcd, int unit) {
     const int P = R - C;
     const int local = j < P ? 2 * j : (j >= C ? 2 * (j - C) + 1 : 2 * P + (j - P));
     return lo + local;
+}
+__device__ __forceinline__ int cu_pair_unit(int cus_per_xcd, int unit) {
+    return cu_pair_renumber(gridDim.x, blockIdx.x, cus_per_xcd, unit);
 }
 
 // Work items per scheduling unit for causal problems (host side).  Query
@@ -227,7 +229,7 @@ inline int causal_items_per_unit(long long items, long long slots, long long sin
 // 2i and 2i + 1 of a head together take the same number of key tiles, so
 // scheduling units of such pairs are all equally long.
 template <bool CAUSAL>
-__device__ __forceinline__ void item_block(int item, int num_qb, int* bh, int* qb) {
+__host__ __device__ __forceinline__ void item_block(int item, int num_qb, int* bh, int* qb) {
     *bh = item / num_qb;
     const int q = item - *bh * num_qb;
     *qb = !CAUSAL ? q : ((q & 1) ? (q >> 1) : num_qb - 1 - (q >> 1));
