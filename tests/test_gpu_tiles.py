@@ -167,6 +167,7 @@ SELECTOR_CASES = [
     ((2, 40, 512, 512, 128, False, False), "bf16_d128_bc64_w8"),         # 1..2 items per CU, whole blocks
     ((32, 3, 302, 302, 128, False, False), "bf16_d128_bc64_w4"),         # same, but 256-row blocks waste rows
     ((1, 10, 8192, 8192, 128, True, False), "bf16_d128_bc64_w8"),        # 2.5 items per CU, long keys
+    ((16, 2, 2671, 2671, 128, True, False), "bf16_d128_bc64_w4"),        # same range, odd 256-row blocks
     ((8, 8, 1024, 1024, 128, True, True), "bf16_d128_bc64_w4"),          # key lengths: no w8
     ((4, 32, 1024, 1024, 128, False, True), "bf16_d128_bc64_w4_pairs"),  # key lengths, > 2 items per CU
     ((8, 8, 512, 2048, 64, False, True), "bf16_d64_bc64_w4_ks2"),        # key lengths, <= 1 item per CU

@@ -37,7 +37,8 @@
 //                         CU).  Only without key lengths and with whole
 //                         256-row blocks where rows would be wasted, it wins
 //                         at d128 non-causal with 1..2 items per CU, at d128
-//                         causal with 2.4..4 items per CU and >= 30 steps, at
+//                         causal with 2.4..4 items per CU, >= 30 steps and an
+//                         even number of 256-row blocks per slice, at
 //                         d64 causal with 3..4.2 items per CU, and at d64
 //                         non-causal from 2 items per CU (where the key split
 //                         does not).
@@ -105,7 +106,12 @@ bool select_bf16_tile(int d, int causal, int has_key_lens, long long bh, int Lq,
         // of query blocks (pairs do not then straddle two slices)
         else if (causal && items <= 2 * cus && steps >= 32 && ((Lq + 127) / 128) % 2 == 0) t = KS2;
         else if (!lens && whole && !causal && items > cus && items <= 2 * cus) t = W8;
-        else if (!lens && causal && 5 * items >= 12 * cus && items <= 4 * cus && steps >= 30) t = W8;
+        // causal 256-row blocks pair up long/short within a slice only when
+        // a slice has an even number of them (measured: 10 of 10 such shapes
+        // faster with w8, 3 of 4 odd ones slower)
+        else if (!lens && causal && 5 * items >= 12 * cus && items <= 4 * cus && steps >= 30 &&
+                 ((Lq + 255) / 256) % 2 == 0)
+            t = W8;
     } else if (causal) {
         if ((items <= cus && steps >= 9) || (items <= 2 * cus && steps >= 20) || steps >= 32) t = KS2;
         else if (!lens && whole && items >= 3 * cus && 5 * items <= 21 * cus) t = W8;
