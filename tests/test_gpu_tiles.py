@@ -177,6 +177,8 @@ SELECTOR_CASES = [
     ((1, 8, 8192, 8192, 64, True, False), "bf16_d64_bc64_w4_ks2"),       # causal, >= 32 key tiles
     ((8, 4, 1280, 1280, 64, True, False), "bf16_d64_bc64_w4_ks2"),       # causal, <= 2 items per CU, 20 tiles
     ((16, 4, 1536, 1536, 64, True, False), "bf16_d64_bc64_w8"),          # causal, 3 items per CU
+    ((8, 8, 2048, 2048, 64, True, False), "bf16_d64_bc64_w8"),           # same at 32 key tiles, even blocks
+    ((8, 12, 1271, 1271, 64, True, False), "bf16_d64_bc64_w4"),          # 3.75 items per CU, 5 blocks: odd
     ((16, 2, 6600, 6600, 64, False, False), "bf16_d64_bc64_w4_ks2"),     # 6.5 items per CU, long keys
     ((64, 16, 512, 512, 64, False, False), "bf16_d64_bc64_w8"),          # many items, whole blocks
 ]

@@ -39,7 +39,9 @@
 //                         at d128 non-causal with 1..2 items per CU, at d128
 //                         causal with 2.4..4 items per CU, >= 30 steps and an
 //                         even number of 256-row blocks per slice, at
-//                         d64 causal with 3..4.2 items per CU, and at d64
+//                         d64 causal with 3..4.2 items per CU (one or an even
+//                         number of 256-row blocks per slice; ahead of the
+//                         key split's 32-step rule), and at d64
 //                         non-causal from 2 items per CU (where the key split
 //                         does not).
 //   bf16_d*_bc64_w4_pairs per-batch key lengths, no causal mask: batches
@@ -113,8 +115,15 @@ bool select_bf16_tile(int d, int causal, int has_key_lens, long long bh, int Lq,
                  ((Lq + 255) / 256) % 2 == 0)
             t = W8;
     } else if (causal) {
-        if ((items <= cus && steps >= 9) || (items <= 2 * cus && steps >= 20) || steps >= 32) t = KS2;
-        else if (!lens && whole && items >= 3 * cus && 5 * items <= 21 * cus) t = W8;
+        // w8 needs one or an even number of 256-row blocks per slice (with an
+        // odd count above one the pairs straddle slices, as at d128: 4 of 5
+        // such shapes slower with w8); where it applies it also beats the
+        // key split from 32 steps (4 of 4 shapes measured)
+        const bool w8 = !lens && whole && items >= 3 * cus && 5 * items <= 21 * cus &&
+                        (((Lq + 255) / 256) % 2 == 0 || Lq <= 256);
+        if ((items <= cus && steps >= 9) || (items <= 2 * cus && steps >= 20)) t = KS2;
+        else if (w8) t = W8;
+        else if (steps >= 32) t = KS2;
     } else {
         if ((items <= cus && steps >= 12) || (steps >= 24 && 2 * items <= 13 * cus)) t = KS2;
         else if (!lens && whole && items > 2 * cus) t = W8;
